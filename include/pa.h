@@ -1,0 +1,181 @@
+/*
+ * pa.h -- C ABI of libpa.so: paged-KV-cache decode attention on MI355X (gfx950).
+ *
+ * Two operations, after the pages this library follows:
+ *
+ *   pa_reshape_and_cache  writes the K and V of new tokens into their cache
+ *                         slots ("vLLM" note, section "PagedAttention": the page
+ *                         holding a token is its position divided by the block
+ *                         size; the cache engine writes pages), optionally
+ *                         quantising to FP8 ("vLLM 前世今生", §5.2 and §7.3).
+ *   pa_decode             one decode step of attention: every sequence's query
+ *                         heads attend over that sequence's cached tokens,
+ *                         reached through its block table ("vLLM 前世今生",
+ *                         §3.2: fixed 16-token blocks, block table, blocks
+ *                         shared between sequences), with grouped-query heads
+ *                         ("vLLM" note, section "内核优化"). The result is
+ *                         softmax(q·Kᵀ·scale)·V per query head.
+ *
+ * Memory and layouts (all arrays dense, row-major, no strides):
+ *   key, value        [num_tokens, num_kv_heads, head_size]          kv_dtype
+ *   k_cache, v_cache  [num_blocks, num_kv_heads, block_size, head_size] cache_dtype
+ *                     (one (block, kv head) tile is block_size*head_size
+ *                      contiguous elements)
+ *   slot_mapping      [num_tokens] int32 or int64; slot = block*block_size + row;
+ *                     a negative slot skips its token
+ *   q                 [num_seqs, num_heads, head_size]                q_dtype
+ *   out               [num_seqs, num_heads, head_size]                out_dtype
+ *   block_tables      [num_seqs, max_blocks_per_seq] int32, physical block ids
+ *   context_lens      [num_seqs] int32, tokens to attend (the newest included)
+ *
+ * Query head h reads KV head h / (num_heads / num_kv_heads).
+ *
+ * Ownership: every pointer is device memory owned by the caller and must stay
+ * valid until the work queued on `stream` has finished. The library never
+ * allocates, frees, copies to the host or synchronises; both calls only queue
+ * kernels on `stream` (a hipStream_t; NULL is the default stream) and return.
+ * They hold no global state besides a thread-local error message and are safe
+ * to call from several threads on different streams.
+ *
+ * Errors: 0 (PA_OK) on success, otherwise a pa_status code, with a message
+ * for the calling thread in pa_last_error(). Arguments are validated on the
+ * host without reading device memory; nothing is launched when validation
+ * fails. Block ids, slots and context lengths are device data and are NOT
+ * checked: an id outside [0, num_blocks), a slot outside
+ * [0, num_blocks*block_size) or a context length above
+ * max_blocks_per_seq*block_size is undefined behaviour (a GPU memory fault).
+ * Launch failures are reported as PA_ERR_LAUNCH; faults inside a kernel
+ * surface at the caller's next synchronisation.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_dtype {
+  PA_DTYPE_F32 = 0,      /* IEEE binary32 */
+  PA_DTYPE_F16 = 1,      /* IEEE binary16 */
+  PA_DTYPE_BF16 = 2,     /* bfloat16 */
+  PA_DTYPE_FP8_E4M3 = 3  /* OCP OFP8 E4M3 (bias 7, max 448, NaN = S.1111.111); caches only */
+} pa_dtype;
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_NULL = 1,         /* a required pointer is NULL */
+  PA_ERR_DTYPE = 2,        /* dtype value or combination not supported */
+  PA_ERR_SHAPE = 3,        /* a size is negative, zero where it must not be, or inconsistent */
+  PA_ERR_UNSUPPORTED = 4,  /* block_size != 16, head_size not 64 or 128, too many query heads per KV head */
+  PA_ERR_WORKSPACE = 5,    /* workspace missing, too small or misaligned */
+  PA_ERR_LAUNCH = 6        /* the HIP runtime rejected a kernel launch */
+} pa_status;
+
+/*
+ * pa_reshape_and_cache -- write new tokens' K and V into cache slots.
+ *
+ * For each token t with slot_mapping[t] >= 0 and each KV head:
+ *   k_cache[slot / block_size, head, slot % block_size, :] = enc(key[t, head, :], k_scale)
+ *   v_cache[...] likewise with value and v_scale.
+ * enc copies the bits when cache_dtype == kv_dtype. With cache_dtype ==
+ * PA_DTYPE_FP8_E4M3 it widens the element to float32, divides by the scale in
+ * float32 (correctly rounded) and rounds to the nearest E4M3 value, ties to
+ * even, saturating to +-448; NaN stays NaN, the sign bit is kept. The scales
+ * are ignored for non-FP8 caches and must be finite and > 0 for FP8.
+ *
+ *   key, value      device, [num_tokens, num_kv_heads, head_size], kv_dtype (F32, F16 or BF16)
+ *   k_cache, v_cache device, [num_blocks, num_kv_heads, block_size, head_size], cache_dtype
+ *                   (== kv_dtype, or FP8_E4M3)
+ *   slot_mapping    device, [num_tokens]; int64 if slot_is_int64 else int32
+ *   num_tokens      >= 0 (0 queues nothing and returns PA_OK)
+ *   block_size      must be 16; head_size must be 64 or 128
+ *
+ * Slots must be distinct within one call (two tokens writing one slot race).
+ */
+int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                         const void* slot_mapping, int slot_is_int64, int64_t num_tokens,
+                         int num_kv_heads, int head_size, int64_t num_blocks, int block_size,
+                         pa_dtype kv_dtype, pa_dtype cache_dtype, float k_scale, float v_scale,
+                         void* stream);
+
+/*
+ * pa_decode -- one decode step of paged attention.
+ *
+ * For every sequence s with n = context_lens[s] and every query head h:
+ *   out[s, h, :] = sum_p w_p V_p / sum_p w_p,  w_p = exp(scale * dot(q[s, h], K_p)),
+ * over token positions p < n, where K_p, V_p are row p % block_size of KV head
+ * h / (num_heads / num_kv_heads) in physical block block_tables[s, p / block_size]
+ * (an FP8 cache's codes are multiplied by k_scale / v_scale). n == 0 writes
+ * zeros. Table entries at and past ceil(n / block_size) are never read, nor
+ * are the rows past n of the last block. Accumulation is float32; out is
+ * rounded to out_dtype to nearest, ties to even.
+ *
+ *   out             device, [num_seqs, num_heads, head_size], out_dtype (q_dtype or F32)
+ *   q               device, [num_seqs, num_heads, head_size], q_dtype (F32, F16 or BF16)
+ *   k_cache, v_cache device, [num_blocks, num_kv_heads, block_size, head_size], cache_dtype
+ *                   (== q_dtype, or FP8_E4M3 with F16 or BF16 queries)
+ *   block_tables    device, int32 [num_seqs, max_blocks_per_seq]
+ *   context_lens    device, int32 [num_seqs], each <= max_blocks_per_seq * block_size
+ *   scale           softmax scale (usually 1/sqrt(head_size)), finite
+ *   num_kv_heads    >= 1 and divides num_heads
+ *   block_size      must be 16; head_size 64 or 128
+ *   workspace       device scratch of at least pa_decode_workspace_bytes(...) bytes,
+ *                   256-byte aligned; may be NULL when that size is 0. Its
+ *                   contents on entry do not matter; it must not be shared with
+ *                   a call running concurrently.
+ *   stream          hipStream_t to queue on
+ *
+ * A context longer than one partition (chosen on the host from the shapes) is
+ * split: each partition writes its running max, sum and unnormalised output
+ * to the workspace, and a second kernel merges the partitions in a fixed
+ * order, so results are deterministic run to run.
+ */
+int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, const int32_t* context_lens, float scale,
+              int num_kv_heads, int block_size, int num_seqs, int num_heads, int head_size,
+              int max_blocks_per_seq, int64_t num_blocks, pa_dtype q_dtype, pa_dtype cache_dtype,
+              pa_dtype out_dtype, float k_scale, float v_scale, void* workspace,
+              size_t workspace_bytes, void* stream);
+
+/*
+ * pa_decode_split -- pa_decode with an explicit partition length.
+ *
+ * partition_blocks = number of 16-token blocks per partition, a multiple of 4
+ * in [4, 1024], or 0 for the library's own choice (then identical to pa_decode).
+ * Results equal pa_decode's up to float32 rounding order. Used to exercise and
+ * time given split factors.
+ */
+int pa_decode_split(void* out, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* context_lens, float scale,
+                    int num_kv_heads, int block_size, int num_seqs, int num_heads, int head_size,
+                    int max_blocks_per_seq, int64_t num_blocks, pa_dtype q_dtype,
+                    pa_dtype cache_dtype, pa_dtype out_dtype, float k_scale, float v_scale,
+                    int partition_blocks, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_decode_workspace_bytes -- workspace size pa_decode / pa_decode_split need
+ * for these shapes (0 when no sequence can span two partitions). Pure
+ * function of its arguments; returns 0 for invalid shapes.
+ * partition_blocks as in pa_decode_split (0 = the library's choice).
+ */
+size_t pa_decode_workspace_bytes(int num_seqs, int num_heads, int num_kv_heads, int head_size,
+                                 int max_blocks_per_seq, int block_size, int partition_blocks);
+
+/* Partition length (in blocks) pa_decode would choose for these shapes. */
+int pa_decode_partition_blocks(int num_seqs, int num_heads, int num_kv_heads, int head_size,
+                               int max_blocks_per_seq, int block_size);
+
+/* Message for the last non-zero status returned on this thread ("" if none). */
+const char* pa_last_error(void);
+
+/* Library version, e.g. "0.1.0". */
+const char* pa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

@@ -1,0 +1,461 @@
+"""Pins of the CPU oracle against things other than itself (no GPU).
+
+Each ``pin_*`` function takes the oracle as a namespace so that the same pin can
+be run against a copy of the oracle with a planted mistake: ``test_mutants``
+shows that every planted mistake is caught by at least one pin.
+"""
+
+import math
+import os
+import types
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from conftest import raw
+from paged_kv_cache_380_amd import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+RAW = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16, "fp8_e4m3": np.uint8}
+
+
+# --- helpers -----------------------------------------------------------------
+
+def to_store(x64: np.ndarray, dtype: str, scale: float = 1.0) -> np.ndarray:
+    """Round float64 data to raw storage with torch's casts (independent of the oracle)."""
+    t = torch.from_numpy(np.ascontiguousarray(x64)).to(torch.float32)
+    if dtype == "fp8_e4m3":
+        t = (t / scale).to(torch.float8_e4m3fn)
+    else:
+        t = t.to(wl.TORCH_DTYPES[dtype])
+    return raw(t)
+
+
+def torch_value(r: np.ndarray, dtype: str, scale: float = 1.0) -> np.ndarray:
+    """Float64 value of raw storage computed by torch's casts (independent of ``widen``)."""
+    if dtype == "bf16":
+        t = torch.from_numpy(r.view(np.int16)).view(torch.bfloat16)
+    elif dtype == "fp8_e4m3":
+        t = torch.from_numpy(r).view(torch.float8_e4m3fn)
+    else:
+        t = torch.from_numpy(r)
+    v = t.to(torch.float64)
+    if dtype == "fp8_e4m3":
+        v = v * float(np.float32(scale))
+    return v.numpy()
+
+
+def filled(O, w: wl.Workload, with_new=True):
+    """Raw caches after writing the cached tokens (and the step's new tokens) with the oracle."""
+    kc, vc = raw(w.poisoned_cache()).copy(), raw(w.poisoned_cache()).copy()
+    O.reshape_and_cache(raw(w.fill_key), raw(w.fill_value), kc, vc, w.fill_slots.numpy(), w.block_size,
+                        w.dtype, w.cache_dtype, w.k_scale, w.v_scale)
+    if with_new:
+        O.reshape_and_cache(raw(w.new_key), raw(w.new_value), kc, vc, w.new_slots.numpy(), w.block_size,
+                            w.dtype, w.cache_dtype, w.k_scale, w.v_scale)
+    return kc, vc
+
+
+def run_decode(O, w, kc, vc, tables=None, lens=None, scale=None, num_kv_heads=None, q=None):
+    return O.decode_attention(raw(w.q) if q is None else q, kc, vc,
+                              w.block_tables.numpy() if tables is None else tables,
+                              w.context_lens.numpy() if lens is None else lens,
+                              w.scale if scale is None else scale,
+                              w.num_kv_heads if num_kv_heads is None else num_kv_heads,
+                              w.block_size, w.dtype, w.cache_dtype, w.k_scale, w.v_scale)
+
+
+def small(seed=0, dtype="f32", cache=None, lens=(1, 5, 16, 17, 40, 33), H=4, Hkv=2, D=8, **kw):
+    return wl.build("small", list(lens), H, Hkv, D, dtype, cache_dtype=cache, seed=seed, free_fraction=0.5,
+                    kv_scale=0.25 if cache == "fp8_e4m3" else 1.0, **kw)
+
+
+# --- pins ------------------------------------------------------------------------
+
+def pin_sdpa_identity_table(O, cache_dtype="f32", q_dtype="f32"):
+    """P1: with an identity block table the oracle equals torch's scaled_dot_product_attention in float64."""
+    rng = np.random.default_rng(11)
+    S, H, Hkv, D, B = 3, 8, 2, 16, 16
+    lens = [1, 23, 70]
+    G = H // Hkv
+    kscale = 0.125 if cache_dtype == "fp8_e4m3" else 1.0
+    vscale = 0.0625 if cache_dtype == "fp8_e4m3" else 1.0
+    nb = [-(-n // B) for n in lens]
+    N = sum(nb)
+    kc = to_store(rng.standard_normal((N, Hkv, B, D)), cache_dtype, kscale)
+    vc = to_store(rng.standard_normal((N, Hkv, B, D)), cache_dtype, vscale)
+    q = to_store(rng.standard_normal((S, H, D)), q_dtype)
+    tables = np.full((S, max(nb)), -1, np.int32)
+    start = 0
+    for s in range(S):
+        tables[s, :nb[s]] = np.arange(start, start + nb[s])
+        start += nb[s]
+    scale = float(np.float32(1 / math.sqrt(D)))
+    out = O.decode_attention(q, kc, vc, tables, np.array(lens, np.int32), scale, Hkv, B, q_dtype, cache_dtype,
+                             kscale, vscale)
+    kv_k = torch_value(kc, cache_dtype, kscale)
+    kv_v = torch_value(vc, cache_dtype, vscale)
+    qv = torch.from_numpy(torch_value(q, q_dtype))
+    for s in range(S):
+        blocks = slice(tables[s, 0], tables[s, 0] + nb[s])
+        # contiguous [Hkv, tokens, D], heads repeated for the grouped queries
+        K = torch.from_numpy(kv_k[blocks]).permute(1, 0, 2, 3).reshape(Hkv, -1, D)[:, :lens[s]]
+        V = torch.from_numpy(kv_v[blocks]).permute(1, 0, 2, 3).reshape(Hkv, -1, D)[:, :lens[s]]
+        K = K.repeat_interleave(G, dim=0)
+        V = V.repeat_interleave(G, dim=0)
+        ref = torch.nn.functional.scaled_dot_product_attention(qv[s][:, None, :], K, V, scale=scale)[:, 0, :]
+        np.testing.assert_allclose(out[s], ref.numpy(), rtol=0, atol=1e-12)
+
+
+def pin_block_permutation(O, cache_dtype="f32", dtype="f32"):
+    """P2: moving physical blocks (and remapping the tables) leaves the output bitwise unchanged."""
+    w = small(seed=3, dtype=dtype, cache=cache_dtype)
+    kc, vc = filled(O, w)
+    out = run_decode(O, w, kc, vc)
+    perm = np.random.default_rng(5).permutation(w.num_blocks)
+    kc2, vc2 = np.empty_like(kc), np.empty_like(vc)
+    kc2[perm], vc2[perm] = kc, vc
+    t = w.block_tables.numpy()
+    t2 = np.where(t >= 0, perm[np.maximum(t, 0)], -1).astype(np.int32)
+    out2 = run_decode(O, w, kc2, vc2, tables=t2)
+    assert np.array_equal(out, out2)
+
+
+def pin_single_token(O, cache_dtype="f32", dtype="f32"):
+    """P3: a context of one token returns that token's V exactly."""
+    w = small(seed=4, dtype=dtype, cache=cache_dtype, lens=(1, 1, 1))
+    kc, vc = filled(O, w)
+    out = run_decode(O, w, kc, vc)
+    for s in range(w.num_seqs):
+        b = int(w.block_tables[s, 0])
+        v = torch_value(vc[b, :, 0, :], w.cache_dtype, w.v_scale)  # [Hkv, D]
+        assert np.array_equal(out[s], np.repeat(v, w.group, axis=0))
+
+
+def pin_equal_keys_give_mean(O):
+    """P4: identical keys (or scale 0) weight every token equally: the output is the mean of V."""
+    w = small(seed=6, lens=(7, 31, 48))
+    kc, vc = filled(O, w)
+    for s in range(w.num_seqs):  # make every key of sequence s equal to its first key
+        n = int(w.context_lens[s])
+        b0 = int(w.block_tables[s, 0])
+        for p in range(n):
+            kc[w.block_tables[s, p // 16], :, p % 16, :] = kc[b0, :, 0, :]
+    for kcache, scale in ((kc, w.scale), (filled(O, w)[0], 0.0)):
+        out = run_decode(O, w, kcache, vc, scale=scale)
+        for s in range(w.num_seqs):
+            n = int(w.context_lens[s])
+            rows = [vc[w.block_tables[s, p // 16], :, p % 16, :].astype(np.float64) for p in range(n)]
+            mean = np.mean(np.stack(rows), axis=0)
+            np.testing.assert_allclose(out[s], np.repeat(mean, w.group, axis=0), rtol=1e-14, atol=1e-15)
+
+
+def pin_two_token_closed_form(O):
+    """P5: with two tokens the output is v0 + sigmoid(l1 - l0) (v1 - v0), l_i = scale * k_i . q."""
+    w = small(seed=7, lens=(2, 2, 2, 2), H=6, Hkv=3)
+    kc, vc = filled(O, w)
+    out = run_decode(O, w, kc, vc)
+    q = raw(w.q).astype(np.float64)
+    for s in range(w.num_seqs):
+        b = int(w.block_tables[s, 0])
+        for h in range(w.num_heads):
+            kv = h // w.group
+            k0, k1 = kc[b, kv, 0].astype(np.float64), kc[b, kv, 1].astype(np.float64)
+            v0, v1 = vc[b, kv, 0].astype(np.float64), vc[b, kv, 1].astype(np.float64)
+            d = w.scale * (k1 @ q[s, h] - k0 @ q[s, h])
+            expect = v0 + (v1 - v0) / (1.0 + math.exp(-d))
+            np.testing.assert_allclose(out[s, h], expect, rtol=1e-13, atol=1e-14)
+
+
+def pin_brute_force(O, dtype="f32", cache_dtype=None):
+    """P6: pure-Python loops (block walk, math.exp, running sums) agree with the oracle."""
+    w = small(seed=8, dtype=dtype, cache=cache_dtype, lens=(3, 16, 29, 40), H=4, Hkv=2, D=4)
+    kc, vc = filled(O, w)
+    out = run_decode(O, w, kc, vc)
+    kv_k = torch_value(kc, w.cache_dtype, w.k_scale)
+    kv_v = torch_value(vc, w.cache_dtype, w.v_scale)
+    qv = torch_value(raw(w.q), w.dtype)
+    for s in range(w.num_seqs):
+        n = int(w.context_lens[s])
+        for h in range(w.num_heads):
+            kv = h * w.num_kv_heads // w.num_heads
+            logits, vals = [], []
+            for j in range(-(-n // 16)):
+                blk = int(w.block_tables[s, j])
+                for o in range(16):
+                    if j * 16 + o >= n:
+                        break
+                    dot = 0.0
+                    for d in range(w.head_size):
+                        dot += float(qv[s, h, d]) * float(kv_k[blk, kv, o, d])
+                    logits.append(w.scale * dot)
+                    vals.append([float(x) for x in kv_v[blk, kv, o]])
+            mx = max(logits)
+            ws = [math.exp(x - mx) for x in logits]
+            tot = sum(ws)
+            expect = [sum(ws[i] * vals[i][d] for i in range(n)) / tot for d in range(w.head_size)]
+            np.testing.assert_allclose(out[s, h], expect, rtol=1e-13, atol=1e-14)
+
+
+def pin_gqa_equals_repeated_mha(O, cache_dtype="f32"):
+    """P7: grouped-query attention equals MHA over KV heads repeated G times, bitwise."""
+    w = small(seed=9, cache=cache_dtype, H=8, Hkv=2)
+    kc, vc = filled(O, w)
+    out = run_decode(O, w, kc, vc)
+    kc_m = np.repeat(kc, w.group, axis=1)
+    vc_m = np.repeat(vc, w.group, axis=1)
+    out_m = run_decode(O, w, kc_m, vc_m, num_kv_heads=w.num_heads)
+    assert np.array_equal(out, out_m)
+
+
+def pin_poison_never_read(O, cache_dtype="f32", dtype="f32"):
+    """P8: NaN in free blocks, past-the-end table entries and unused tail rows never reaches the output."""
+    w = small(seed=10, dtype=dtype, cache=cache_dtype, lens=(1, 15, 17, 33))
+    kc, vc = filled(O, w)  # everything not written holds NaN (the workload poisons the pool)
+    tables = w.block_tables.numpy().copy()
+    nan_block = int(np.setdiff1d(np.arange(w.num_blocks), tables[tables >= 0])[0])
+    tables[tables < 0] = nan_block  # padding now points at a poisoned block
+    out = run_decode(O, w, kc, vc, tables=tables)
+    assert np.isfinite(out).all()
+
+
+def pin_reshape_round_trip(O, dtype="bf16"):
+    """P9: scattering tokens then gathering them through their slots returns the input bitwise."""
+    w = small(seed=12, dtype=dtype, lens=(5, 16, 33, 48))
+    kc, vc = filled(O, w, with_new=False)
+    slots = w.fill_slots.numpy()
+    k_back = kc[slots // 16, :, slots % 16, :]
+    v_back = vc[slots // 16, :, slots % 16, :]
+    assert np.array_equal(k_back.view(np.uint8), raw(w.fill_key).view(np.uint8))
+    assert np.array_equal(v_back.view(np.uint8), raw(w.fill_value).view(np.uint8))
+
+
+def pin_reshape_locality(O, dtype="f16", cache_dtype=None):
+    """P10: bytes no valid slot addresses keep their previous contents; negative slots write nothing."""
+    w = small(seed=13, dtype=dtype, cache=cache_dtype, lens=(9, 21))
+    rng = np.random.default_rng(1)
+    kc0 = rng.integers(0, 256, size=np.prod(w.cache_shape()) * np.dtype(RAW[w.cache_dtype]).itemsize,
+                       dtype=np.uint8).view(RAW[w.cache_dtype]).reshape(w.cache_shape())
+    kc, vc = kc0.copy(), kc0.copy()
+    slots = w.fill_slots.numpy().copy()
+    slots[::3] = -1
+    O.reshape_and_cache(raw(w.fill_key), raw(w.fill_value), kc, vc, slots, 16, w.dtype, w.cache_dtype,
+                        w.k_scale, w.v_scale)
+    touched = np.zeros(w.cache_shape(), bool)
+    good = slots[slots >= 0]
+    touched[good // 16, :, good % 16, :] = True
+    assert np.array_equal(kc[~touched].view(np.uint8), kc0[~touched].view(np.uint8))
+    assert np.array_equal(vc[~touched].view(np.uint8), kc0[~touched].view(np.uint8))
+    assert not np.array_equal(kc[touched].view(np.uint8), kc0[touched].view(np.uint8))
+
+
+def pin_e4m3_golden(O):
+    """P11a: the code table holds the code points printed in the OCP OFP8 specification."""
+    vals = O.e4m3_code_values()
+    with open(os.path.join(GOLDEN, "ocp_e4m3_code_points.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].split()
+            if not line:
+                continue
+            code, v = int(line[0], 16), float(line[1])
+            if math.isnan(v):
+                assert math.isnan(vals[code])
+            else:
+                assert vals[code] == v and math.copysign(1, vals[code]) == math.copysign(1, v), hex(code)
+    finite = vals[~np.isnan(vals)]
+    assert len(finite) == 254 and finite.max() == 448.0 and finite.min() == -448.0
+
+
+def pin_e4m3_nearest_even(O):
+    """P11b: the encoder picks the nearest grid value (ties: even code), brute-forced over the grid."""
+    vals = O.e4m3_code_values()
+    pos = np.arange(0x7F)
+    rng = np.random.default_rng(2)
+    grid = vals[pos]
+    mids = (grid[:-1] + grid[1:]) / 2
+    x = np.concatenate([grid, mids, rng.uniform(0, 448, 4000), 2.0 ** rng.uniform(-12, 8.8, 4000)])
+    x = x[x <= 448].astype(np.float32)
+    x = np.concatenate([x, -x])
+    codes = O.e4m3_encode(x)
+    for xi, c in zip(x.astype(np.float64), codes):
+        dist = np.abs(grid - abs(xi))
+        best = np.flatnonzero(dist == dist.min())
+        if len(best) == 2:
+            best = best[(best & 1) == 0]
+        assert (c & 0x7F) == best[0], (xi, hex(c))
+        assert (c >> 7) == (1 if np.signbit(xi) else 0)
+
+
+def pin_e4m3_vs_torch(O):
+    """P11c: encoding agrees with torch's float8_e4m3fn cast on every bf16 input / 0.05 up to 464."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    x = (bits.astype(np.uint32) << 16).view(np.float32)
+    with np.errstate(over="ignore", invalid="ignore"):
+        y = np.divide(x, np.float32(0.05), dtype=np.float32)
+    keep = np.isfinite(y) & (np.abs(y) <= 464)
+    y = y[keep]
+    ours = O.e4m3_encode(y)
+    theirs = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(ours, theirs)
+    # saturation and specials (torch does not saturate past 464, so these are checked by value)
+    sp = np.array([449, 464, 470, 1e6, np.inf, -np.inf, np.nan, -0.0, 2.0 ** -11, -(2.0 ** -11),
+                   2.0 ** -10, 3 * 2.0 ** -10], np.float32)
+    assert list(O.e4m3_encode(sp)) == [0x7E, 0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0x7F, 0x80, 0x00, 0x80, 0x00, 0x02]
+
+
+def pin_fp8_cache_quantisation(O):
+    """P11d: an fp8 cache stores the nearest E4M3 code of the float32 quotient x / scale."""
+    w = small(seed=14, dtype="bf16", cache="fp8_e4m3", lens=(20, 3))
+    kc, _ = filled(O, w, with_new=False)
+    slots = w.fill_slots.numpy()
+    codes = kc[slots // 16, :, slots % 16, :]
+    x = torch.from_numpy(raw(w.fill_key).view(np.int16)).view(torch.bfloat16).to(torch.float32)
+    y = (x / torch.tensor(w.k_scale, dtype=torch.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(codes, y)
+
+
+PINS = [
+    pin_sdpa_identity_table, pin_block_permutation, pin_single_token, pin_equal_keys_give_mean,
+    pin_two_token_closed_form, pin_brute_force, pin_gqa_equals_repeated_mha, pin_poison_never_read,
+    pin_reshape_round_trip, pin_reshape_locality, pin_e4m3_golden, pin_e4m3_nearest_even, pin_e4m3_vs_torch,
+    pin_fp8_cache_quantisation,
+]
+
+
+# --- tests -----------------------------------------------------------------------
+
+@pytest.mark.parametrize("cache,qd", [("f32", "f32"), ("f16", "f16"), ("bf16", "bf16"), ("fp8_e4m3", "bf16"),
+                                      ("fp8_e4m3", "f16")])
+def test_p1_sdpa_identity_table(cache, qd):
+    pin_sdpa_identity_table(oracle, cache, qd)
+
+
+@pytest.mark.parametrize("dtype,cache", [("f32", None), ("bf16", None), ("bf16", "fp8_e4m3")])
+def test_p2_block_permutation(dtype, cache):
+    pin_block_permutation(oracle, cache or dtype, dtype)
+
+
+@pytest.mark.parametrize("dtype,cache", [("f32", None), ("f16", None), ("bf16", None), ("bf16", "fp8_e4m3")])
+def test_p3_single_token(dtype, cache):
+    pin_single_token(oracle, cache or dtype, dtype)
+
+
+def test_p4_equal_keys_give_mean():
+    pin_equal_keys_give_mean(oracle)
+
+
+def test_p5_two_token_closed_form():
+    pin_two_token_closed_form(oracle)
+
+
+@pytest.mark.parametrize("dtype,cache", [("f32", None), ("bf16", "fp8_e4m3")])
+def test_p6_brute_force(dtype, cache):
+    pin_brute_force(oracle, dtype, cache)
+
+
+@pytest.mark.parametrize("cache", ["f32", "fp8_e4m3"])
+def test_p7_gqa_equals_repeated_mha(cache):
+    if cache == "fp8_e4m3":
+        w = small(seed=9, dtype="bf16", cache=cache, H=8, Hkv=2)
+        kc, vc = filled(oracle, w)
+        out = run_decode(oracle, w, kc, vc)
+        out_m = run_decode(oracle, w, np.repeat(kc, 4, 1), np.repeat(vc, 4, 1), num_kv_heads=8)
+        assert np.array_equal(out, out_m)
+    else:
+        pin_gqa_equals_repeated_mha(oracle, cache)
+
+
+@pytest.mark.parametrize("dtype,cache", [("f32", None), ("f16", None), ("bf16", "fp8_e4m3")])
+def test_p8_poison_never_read(dtype, cache):
+    pin_poison_never_read(oracle, cache or dtype, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_p9_reshape_round_trip(dtype):
+    pin_reshape_round_trip(oracle, dtype)
+
+
+@pytest.mark.parametrize("dtype,cache", [("f16", None), ("bf16", "fp8_e4m3")])
+def test_p10_reshape_locality(dtype, cache):
+    pin_reshape_locality(oracle, dtype, cache)
+
+
+def test_p11_e4m3():
+    pin_e4m3_golden(oracle)
+    pin_e4m3_nearest_even(oracle)
+    pin_e4m3_vs_torch(oracle)
+    pin_fp8_cache_quantisation(oracle)
+
+
+def test_zero_context_gives_zeros():
+    w = small(seed=15, lens=(0, 4, 0))
+    kc, vc = filled(oracle, w)
+    out = run_decode(oracle, w, kc, vc)
+    assert np.array_equal(out[0], np.zeros_like(out[0])) and np.array_equal(out[2], np.zeros_like(out[2]))
+    assert np.isfinite(out).all()
+
+
+# --- planted mistakes ----------------------------------------------------------------
+
+MUTANTS = {
+    "gqa head map h % Hkv": ("kv = h // group", "kv = h % num_kv_heads"),
+    "row index p // B": ("rows = pos % block_size", "rows = pos // block_size % block_size"),
+    "scale dropped": ("logits = scale64 * (", "logits = 1.0 * ("),
+    "max not subtracted, exp of neg": ("np.exp(logits - logits.max())", "np.exp(-(logits - logits.max()))"),
+    "normaliser dropped": ("/ weights.sum()", "/ len(weights)"),
+    "V read with the K scale": ("values = widen(v_cache[phys, :, rows, :], cache_dtype, v_scale)",
+                                "values = widen(v_cache[phys, :, rows, :], cache_dtype, k_scale)"),
+    "slot offset off by one": ("offsets = slots[valid] % block_size", "offsets = (slots[valid] + 1) % block_size"),
+    "q/K transposed heads": ("qs = widen(q[s], q_dtype)", "qs = widen(q[s], q_dtype)[::-1]"),
+    "e4m3 bias 8": ("2.0 ** (exp_field - 7)", "2.0 ** (exp_field - 8)"),
+    "e4m3 round half up": ("mag = np.rint(a / quantum) * quantum", "mag = np.floor(a / quantum + 0.5) * quantum"),
+    "e4m3 no saturation": ("mag = np.where(a > E4M3_MAX, E4M3_MAX, mag)", "mag = np.where(a > E4M3_MAX, 0.0, mag)"),
+}
+
+
+def _mutant(find: str, repl: str) -> types.SimpleNamespace:
+    """A private copy of the oracle with one source substitution (the plant is made in the oracle, on the CPU)."""
+    here = os.path.dirname(oracle.__file__)
+    src_e = open(os.path.join(here, "e4m3.py")).read()
+    src_p = open(os.path.join(here, "paged_attention.py")).read()
+    hit = (find in src_e) + (find in src_p)
+    assert hit == 1, find
+    src_e, src_p = src_e.replace(find, repl), src_p.replace(find, repl)
+    e = types.ModuleType("mut_e4m3")
+    exec(compile(src_e, "mut_e4m3", "exec"), e.__dict__)
+    p = types.ModuleType("mut_pa")
+    p.__dict__["__name__"] = "mut_pa"
+    src_p = src_p.replace("from .e4m3 import e4m3_decode, e4m3_encode", "")
+    p.__dict__.update(e4m3_decode=e.e4m3_decode, e4m3_encode=e.e4m3_encode)
+    exec(compile(src_p, "mut_pa", "exec"), p.__dict__)
+    return types.SimpleNamespace(
+        decode_attention=p.decode_attention, reshape_and_cache=p.reshape_and_cache, widen=p.widen,
+        e4m3_code_values=e.e4m3_code_values, e4m3_encode=e.e4m3_encode, e4m3_decode=e.e4m3_decode)
+
+
+def _runs_clean(O) -> bool:
+    variants = [
+        lambda: pin_sdpa_identity_table(O), lambda: pin_sdpa_identity_table(O, "fp8_e4m3", "bf16"),
+        lambda: pin_block_permutation(O), lambda: pin_single_token(O, "fp8_e4m3", "bf16"),
+        lambda: pin_equal_keys_give_mean(O), lambda: pin_two_token_closed_form(O), lambda: pin_brute_force(O),
+        lambda: pin_gqa_equals_repeated_mha(O), lambda: pin_reshape_round_trip(O),
+        lambda: pin_reshape_locality(O), lambda: pin_e4m3_golden(O), lambda: pin_e4m3_vs_torch(O),
+        lambda: pin_fp8_cache_quantisation(O),
+    ]
+    for v in variants:
+        try:
+            v()
+        except (AssertionError, ValueError, IndexError, FloatingPointError):
+            return False
+    return True
+
+
+def test_unmutated_copy_passes():
+    assert _runs_clean(_mutant("E4M3_MAX = 448.0", "E4M3_MAX = 448.0"))
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutants(name):
+    assert not _runs_clean(_mutant(*MUTANTS[name])), f"planted mistake '{name}' not caught by any pin"
