@@ -144,7 +144,7 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
  * pa_decode_split -- pa_decode with an explicit partition length.
  *
  * partition_blocks = number of 16-token blocks per partition, a multiple of 4
- * in [4, 1024], or 0 for the library's own choice (then identical to pa_decode).
+ * in [4, 512], or 0 for the library's own choice (then identical to pa_decode).
  * Results equal pa_decode's up to float32 rounding order. Used to exercise and
  * time given split factors.
  */

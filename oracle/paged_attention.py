@@ -60,8 +60,10 @@ def quantize_for_cache(x_raw: np.ndarray, src_dtype: str, cache_dtype: str, scal
     """What reshape-and-cache stores for activations ``x_raw``.
 
     Same dtype: the bits are copied. FP8 cache ([vLLM-history] §5.2): the value
-    is widened to float32 (exact), divided by the float32 scale with one
-    correctly rounded float32 division, and encoded to E4M3 (RNE, saturating).
+    is widened to float32 (exact), its magnitude divided by the float32 scale
+    with one correctly rounded float32 division, the input's sign bit put back
+    (so a NaN keeps its sign too; for every other input this equals x / scale),
+    and the quotient encoded to E4M3 (RNE, saturating).
     """
     _check_raw(x_raw, src_dtype)
     if cache_dtype == src_dtype:
@@ -69,7 +71,8 @@ def quantize_for_cache(x_raw: np.ndarray, src_dtype: str, cache_dtype: str, scal
     if cache_dtype != "fp8_e4m3" or src_dtype == "fp8_e4m3":
         raise ValueError(f"cannot store {src_dtype} activations in a {cache_dtype} cache")
     x32 = widen(x_raw, src_dtype).astype(np.float32)  # exact: every source dtype fits in float32
-    y = np.divide(x32, np.float32(scale), dtype=np.float32)
+    with np.errstate(invalid="ignore", over="ignore"):
+        y = np.copysign(np.divide(np.abs(x32), np.float32(scale), dtype=np.float32), x32)
     return e4m3_encode(y)
 
 

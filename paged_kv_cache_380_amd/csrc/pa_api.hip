@@ -1,0 +1,213 @@
+// C ABI of libpa.so (declared and documented in include/pa.h): argument
+// validation on the host, partition and workspace sizing, kernel dispatch.
+// Nothing here reads device memory, allocates or synchronises.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "pa.h"
+#include "pa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return PA_OK;
+}
+
+bool activation_kind(int k) { return k == PA_DTYPE_F32 || k == PA_DTYPE_F16 || k == PA_DTYPE_BF16; }
+
+// Workgroups wanted before a context is split: with 256 compute units this
+// keeps every unit several workgroups deep.
+constexpr int64_t kTargetWorkgroups = 1024;
+
+int choose_partition_blocks(int num_seqs, int num_heads, int num_kv_heads, int max_blocks) {
+  const int group = num_heads / num_kv_heads;
+  const int64_t tiles = (int64_t)num_seqs * num_kv_heads * (group / pa::group_tile_for(group));
+  int64_t parts = 1;
+  if (tiles > 0 && tiles < kTargetWorkgroups) parts = (kTargetWorkgroups + tiles - 1) / tiles;
+  int64_t pb = (max_blocks + parts - 1) / parts;
+  pb = (pb + 3) / 4 * 4;
+  if (pb < 4) pb = 4;
+  if (pb > pa::kMaxPartitionBlocks) pb = pa::kMaxPartitionBlocks;
+  return (int)pb;
+}
+
+bool shapes_ok(int num_seqs, int num_heads, int num_kv_heads, int head_size, int max_blocks, int block_size) {
+  return num_seqs >= 0 && num_seqs <= 65535 && num_heads >= 1 && num_kv_heads >= 1 &&
+         num_heads % num_kv_heads == 0 && (head_size == 64 || head_size == 128) && max_blocks >= 1 &&
+         block_size == 16;
+}
+
+struct Layout {
+  int partition_blocks;
+  int num_parts;
+  size_t out_bytes;  // partition outputs, at offset 0
+  size_t ml_offset;  // partition max/sum pairs
+  size_t total;
+};
+
+Layout workspace_layout(int num_seqs, int num_heads, int head_size, int max_blocks, int pb) {
+  Layout L{};
+  L.partition_blocks = pb;
+  L.num_parts = (max_blocks + pb - 1) / pb;
+  if (L.num_parts <= 1 || num_seqs == 0) return L;
+  const size_t rows = (size_t)num_seqs * num_heads * L.num_parts;
+  L.out_bytes = rows * head_size * sizeof(float);
+  L.ml_offset = (L.out_bytes + 255) / 256 * 256;
+  L.total = L.ml_offset + rows * 2 * sizeof(float);
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_last_error(void) { return g_last_error.c_str(); }
+
+const char* pa_version(void) { return "0.1.0"; }
+
+int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                         const void* slot_mapping, int slot_is_int64, int64_t num_tokens,
+                         int num_kv_heads, int head_size, int64_t num_blocks, int block_size,
+                         pa_dtype kv_dtype, pa_dtype cache_dtype, float k_scale, float v_scale,
+                         void* stream) {
+  if (num_tokens < 0 || num_kv_heads < 1 || num_blocks < 1)
+    return fail(PA_ERR_SHAPE, "reshape_and_cache: bad sizes (num_tokens=%lld, num_kv_heads=%d, num_blocks=%lld)",
+                (long long)num_tokens, num_kv_heads, (long long)num_blocks);
+  if (block_size != 16)
+    return fail(PA_ERR_UNSUPPORTED, "reshape_and_cache: block_size must be 16 (got %d)", block_size);
+  if (head_size != 64 && head_size != 128)
+    return fail(PA_ERR_UNSUPPORTED, "reshape_and_cache: head_size must be 64 or 128 (got %d)", head_size);
+  if (!activation_kind(kv_dtype))
+    return fail(PA_ERR_DTYPE, "reshape_and_cache: key/value dtype must be F32, F16 or BF16");
+  if (cache_dtype != kv_dtype && cache_dtype != PA_DTYPE_FP8_E4M3)
+    return fail(PA_ERR_DTYPE, "reshape_and_cache: cache dtype must equal the key dtype or be FP8_E4M3");
+  if (cache_dtype == PA_DTYPE_FP8_E4M3 &&
+      !(std::isfinite(k_scale) && std::isfinite(v_scale) && k_scale > 0.f && v_scale > 0.f))
+    return fail(PA_ERR_SHAPE, "reshape_and_cache: FP8 scales must be finite and positive");
+  if (num_tokens == 0) return ok();
+  if (!key || !value || !k_cache || !v_cache || !slot_mapping)
+    return fail(PA_ERR_NULL, "reshape_and_cache: NULL pointer argument");
+  pa::ReshapeArgs a{key, value, k_cache, v_cache, slot_mapping, num_tokens, num_kv_heads, head_size,
+                    slot_is_int64 ? 1 : 0, k_scale, v_scale};
+  const hipError_t e = pa::launch_reshape(a, kv_dtype, cache_dtype, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "reshape_and_cache: launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int pa_decode_partition_blocks(int num_seqs, int num_heads, int num_kv_heads, int head_size,
+                               int max_blocks_per_seq, int block_size) {
+  if (!shapes_ok(num_seqs, num_heads, num_kv_heads, head_size, max_blocks_per_seq, block_size)) return 0;
+  return choose_partition_blocks(num_seqs, num_heads, num_kv_heads, max_blocks_per_seq);
+}
+
+size_t pa_decode_workspace_bytes(int num_seqs, int num_heads, int num_kv_heads, int head_size,
+                                 int max_blocks_per_seq, int block_size, int partition_blocks) {
+  if (!shapes_ok(num_seqs, num_heads, num_kv_heads, head_size, max_blocks_per_seq, block_size)) return 0;
+  if (partition_blocks == 0)
+    partition_blocks = choose_partition_blocks(num_seqs, num_heads, num_kv_heads, max_blocks_per_seq);
+  if (partition_blocks < 4 || partition_blocks > pa::kMaxPartitionBlocks || partition_blocks % 4) return 0;
+  return workspace_layout(num_seqs, num_heads, head_size, max_blocks_per_seq, partition_blocks).total;
+}
+
+int pa_decode_split(void* out, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* context_lens, float scale,
+                    int num_kv_heads, int block_size, int num_seqs, int num_heads, int head_size,
+                    int max_blocks_per_seq, int64_t num_blocks, pa_dtype q_dtype,
+                    pa_dtype cache_dtype, pa_dtype out_dtype, float k_scale, float v_scale,
+                    int partition_blocks, void* workspace, size_t workspace_bytes, void* stream) {
+  if (block_size != 16) return fail(PA_ERR_UNSUPPORTED, "decode: block_size must be 16 (got %d)", block_size);
+  if (head_size != 64 && head_size != 128)
+    return fail(PA_ERR_UNSUPPORTED, "decode: head_size must be 64 or 128 (got %d)", head_size);
+  if (num_seqs < 0 || num_seqs > 65535 || num_heads < 1 || num_kv_heads < 1 || max_blocks_per_seq < 1 ||
+      num_blocks < 1)
+    return fail(PA_ERR_SHAPE,
+                "decode: bad sizes (num_seqs=%d in [0,65535], num_heads=%d, num_kv_heads=%d, "
+                "max_blocks_per_seq=%d, num_blocks=%lld)",
+                num_seqs, num_heads, num_kv_heads, max_blocks_per_seq, (long long)num_blocks);
+  if (num_heads % num_kv_heads)
+    return fail(PA_ERR_SHAPE, "decode: num_heads (%d) is not a multiple of num_kv_heads (%d)", num_heads,
+                num_kv_heads);
+  if (!activation_kind(q_dtype)) return fail(PA_ERR_DTYPE, "decode: q dtype must be F32, F16 or BF16");
+  const bool fp8 = cache_dtype == PA_DTYPE_FP8_E4M3;
+  if (!(cache_dtype == q_dtype || (fp8 && q_dtype != PA_DTYPE_F32)))
+    return fail(PA_ERR_DTYPE, "decode: cache dtype must equal the q dtype, or be FP8_E4M3 with F16/BF16 queries");
+  if (out_dtype != q_dtype && out_dtype != PA_DTYPE_F32)
+    return fail(PA_ERR_DTYPE, "decode: out dtype must be the q dtype or F32");
+  if (!std::isfinite(scale)) return fail(PA_ERR_SHAPE, "decode: scale must be finite");
+  if (fp8 && !(std::isfinite(k_scale) && std::isfinite(v_scale) && k_scale > 0.f && v_scale > 0.f))
+    return fail(PA_ERR_SHAPE, "decode: FP8 scales must be finite and positive");
+  if (partition_blocks != 0 &&
+      (partition_blocks < 4 || partition_blocks > pa::kMaxPartitionBlocks || partition_blocks % 4))
+    return fail(PA_ERR_UNSUPPORTED, "decode: partition_blocks must be 0 or a multiple of 4 in [4, %d] (got %d)",
+                pa::kMaxPartitionBlocks, partition_blocks);
+  if (num_seqs == 0) return ok();
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return fail(PA_ERR_NULL, "decode: NULL pointer argument");
+
+  const int pb = partition_blocks ? partition_blocks
+                                  : choose_partition_blocks(num_seqs, num_heads, num_kv_heads, max_blocks_per_seq);
+  const Layout L = workspace_layout(num_seqs, num_heads, head_size, max_blocks_per_seq, pb);
+  if (L.num_parts > 65535) return fail(PA_ERR_UNSUPPORTED, "decode: too many partitions (%d)", L.num_parts);
+  if (L.total > 0) {
+    if (!workspace)
+      return fail(PA_ERR_WORKSPACE, "decode: a workspace of %zu bytes is needed", L.total);
+    if (workspace_bytes < L.total)
+      return fail(PA_ERR_WORKSPACE, "decode: workspace of %zu bytes is smaller than the %zu needed", workspace_bytes,
+                  L.total);
+    if (reinterpret_cast<uintptr_t>(workspace) % 256)
+      return fail(PA_ERR_WORKSPACE, "decode: workspace must be 256-byte aligned");
+  }
+
+  pa::DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.ws_out = L.total ? static_cast<float*>(workspace) : nullptr;
+  a.ws_ml = L.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + L.ml_offset) : nullptr;
+  const double log2e = 1.4426950408889634;
+  a.qk_scale = (float)((double)scale * log2e * (fp8 ? (double)k_scale : 1.0));
+  a.out_scale = fp8 ? v_scale : 1.0f;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_size = head_size;
+  a.group = num_heads / num_kv_heads;
+  a.group_tile = pa::group_tile_for(a.group);
+  a.max_blocks = max_blocks_per_seq;
+  a.partition_blocks = pb;
+  a.num_parts = L.num_parts;
+  a.out_kind = out_dtype;
+  const hipError_t e = pa::launch_decode(a, q_dtype, cache_dtype, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "decode: launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+              const int32_t* context_lens, float scale, int num_kv_heads, int block_size, int num_seqs,
+              int num_heads, int head_size, int max_blocks_per_seq, int64_t num_blocks, pa_dtype q_dtype,
+              pa_dtype cache_dtype, pa_dtype out_dtype, float k_scale, float v_scale, void* workspace,
+              size_t workspace_bytes, void* stream) {
+  return pa_decode_split(out, q, k_cache, v_cache, block_tables, context_lens, scale, num_kv_heads, block_size,
+                         num_seqs, num_heads, head_size, max_blocks_per_seq, num_blocks, q_dtype, cache_dtype,
+                         out_dtype, k_scale, v_scale, 0, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

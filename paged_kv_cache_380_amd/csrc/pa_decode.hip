@@ -1,0 +1,393 @@
+// Paged-attention decode for gfx950 (CDNA4).
+//
+// What is computed ("vLLM 前世今生" §3.2; "vLLM" note, sections "PagedAttention"
+// and "内核优化"): for every sequence and query head, softmax(q·Kᵀ·scale)·V
+// over the sequence's cached tokens, which sit in 16-token blocks scattered
+// through a pool and are reached through the sequence's block table; a group
+// of query heads shares one KV head.
+//
+// How (decode is a matrix-vector product, bound by HBM bandwidth, so no MFMA):
+//  * one workgroup of 4 waves per (sequence, KV head, head tile, partition);
+//    all query heads of the tile are served from one read of each K/V tile;
+//  * the partition's slice of the block table is staged in LDS; each wave walks
+//    its share of the blocks (wave w takes blocks w, w+4, ...), reading each
+//    (block, KV head) tile of 16 rows with 16-byte loads: one wave-load moves
+//    1 KiB of contiguous memory, and the next tile's loads are issued before
+//    the current tile is consumed;
+//  * a token row is split over LPR lanes; q·k is a packed dot product per lane
+//    (v_dot2 for 16-bit data) followed by a DPP butterfly inside the lane group;
+//  * every lane group keeps its own running max / sum / output (the online
+//    softmax normaliser of Milakov & Gimelshein, 2018, also used by
+//    FlashAttention, which the history page cites in §2.2); the groups and
+//    the waves are merged once at the end through shuffles and LDS;
+//  * a context longer than one partition is split: each partition leaves its
+//    max, sum and unnormalised output in the workspace and decode_reduce merges
+//    them in partition order (deterministic).
+// Rows past the context (the tail of the last block) are removed by selection,
+// never by multiplying with zero, so stale or NaN data there cannot leak.
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+template <int QK, int CK, int D> struct QFrag {
+  static constexpr int kElems = TileGeo<CK, D>::E;                     // q elements per lane
+  static constexpr int kWords = (QK == kF32) ? kElems : kElems / 2;    // 32-bit words per lane
+};
+
+// Partial q·k over the E elements one lane holds of a token row.
+template <int QK, int CK>
+__device__ __forceinline__ float dot_chunk(const uint32_t* qw, const uint4& k) {
+  const uint32_t kw[4] = {k.x, k.y, k.z, k.w};
+  float acc = 0.f;
+  if constexpr (CK == kF32) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc = __builtin_fmaf(__uint_as_float(qw[i]), __uint_as_float(kw[i]), acc);
+  } else if constexpr (CK == kF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, qw[i]), __builtin_bit_cast(half2_t, kw[i]), acc, false);
+  } else if constexpr (CK == kBF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, qw[i]), __builtin_bit_cast(bf162_t, kw[i]),
+                                            acc, false);
+  } else {
+    // FP8 codes widen exactly to the query's 16-bit type (scale 1), then dot2.
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (QK == kBF16) {
+        const bf162_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)kw[i], 1.0f, false);
+        const bf162_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)kw[i], 1.0f, true);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, qw[2 * i]), lo, acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, qw[2 * i + 1]), hi, acc, false);
+      } else {
+        const half2_t lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)kw[i], 1.0f, false);
+        const half2_t hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)kw[i], 1.0f, true);
+        acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, qw[2 * i]), lo, acc, false);
+        acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, qw[2 * i + 1]), hi, acc, false);
+      }
+    }
+  }
+  return acc;
+}
+
+// The E elements one lane holds of a V row, as float32.
+template <int CK>
+__device__ __forceinline__ void v_to_float(const uint4& v, float* f) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (CK == kF32) {
+      f[i] = __uint_as_float(w[i]);
+    } else if constexpr (CK == kF16) {
+      f[2 * i] = f16_lo(w[i]);
+      f[2 * i + 1] = f16_hi(w[i]);
+    } else if constexpr (CK == kBF16) {
+      f[2 * i] = bf16_lo(w[i]);
+      f[2 * i + 1] = bf16_hi(w[i]);
+    } else {
+      const float2_t lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)w[i], 1.0f, false);
+      const float2_t hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)w[i], 1.0f, true);
+      f[4 * i] = lo.x;
+      f[4 * i + 1] = lo.y;
+      f[4 * i + 2] = hi.x;
+      f[4 * i + 3] = hi.y;
+    }
+  }
+}
+
+__device__ __forceinline__ void store_out(const DecodeArgs& a, int64_t elem, float x) {
+  if (a.out_kind == kF32) {
+    static_cast<float*>(a.out)[elem] = x;
+  } else if (a.out_kind == kBF16) {
+    static_cast<uint16_t*>(a.out)[elem] = f32_to_bf16_rne(x);
+  } else {
+    static_cast<uint16_t*>(a.out)[elem] = f32_to_f16_rne(x);
+  }
+}
+
+template <int QK, int CK, int D, int GT>
+__global__ __launch_bounds__(kThreads) void decode_main(const DecodeArgs a) {
+  using Geo = TileGeo<CK, D>;
+  constexpr int E = Geo::E, LPR = Geo::LPR, RPL = Geo::RPL, NL = Geo::NL;
+  constexpr int QW = QFrag<QK, CK, D>::kWords;
+  constexpr int kQBytes = KindBytes<QK>::value;
+  constexpr int kTileBytes = 16 * D * Geo::kBytes;
+  static_assert(RPL * D * Geo::kBytes == 1024, "a wave-load covers 1 KiB");
+
+  __shared__ int s_blocks[kMaxPartitionBlocks];
+  __shared__ float s_acc[kWaves][GT][D];
+  __shared__ float s_ml[kWaves][GT][2];
+
+  const int n_sub = a.group / GT;
+  const int kvh = blockIdx.x / n_sub;
+  const int h0 = kvh * a.group + (blockIdx.x - kvh * n_sub) * GT;  // first query head of the tile
+  const int part = blockIdx.y;
+  const int seq = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+
+  const int ctx = a.context_lens[seq];
+  if (ctx <= 0) {  // nothing to attend: zeros, written once by partition 0
+    if (part == 0)
+      for (int idx = tid; idx < GT * D; idx += kThreads)
+        store_out(a, ((int64_t)seq * a.num_heads + h0) * D + idx, 0.f);
+    return;
+  }
+  const int seq_blocks = (ctx + 15) >> 4;
+  const int blk0 = part * a.partition_blocks;
+  if (blk0 >= seq_blocks) return;
+  const int nblk = min(a.partition_blocks, seq_blocks - blk0);
+  const int seq_parts = (seq_blocks + a.partition_blocks - 1) / a.partition_blocks;
+
+  const int32_t* bt = a.block_tables + (int64_t)seq * a.max_blocks + blk0;
+  for (int j = tid; j < nblk; j += kThreads) s_blocks[j] = bt[j];
+
+  const int col = lane % LPR;  // which E-element slice of a row this lane holds
+  const int row = lane / LPR;  // which of the RPL rows of a wave-load
+
+  uint32_t qf[GT][QW];
+  {
+    const char* qp = static_cast<const char*>(a.q) + (((int64_t)seq * a.num_heads + h0) * D + col * E) * kQBytes;
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+#pragma unroll
+      for (int c = 0; c < QW / 4; ++c) {
+        const uint4 v = *reinterpret_cast<const uint4*>(qp + g * D * kQBytes + c * 16);
+        qf[g][4 * c] = v.x;
+        qf[g][4 * c + 1] = v.y;
+        qf[g][4 * c + 2] = v.z;
+        qf[g][4 * c + 3] = v.w;
+      }
+    }
+  }
+  __syncthreads();
+
+  float m[GT], l[GT], acc[GT][E];
+#pragma unroll
+  for (int g = 0; g < GT; ++g) {
+    m[g] = kNegInf;
+    l[g] = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[g][e] = 0.f;
+  }
+
+  const int64_t blk_stride = (int64_t)a.num_kv_heads * kTileBytes;
+  const char* kbase = static_cast<const char*>(a.k_cache) + (int64_t)kvh * kTileBytes + lane * 16;
+  const char* vbase = static_cast<const char*>(a.v_cache) + (int64_t)kvh * kTileBytes + lane * 16;
+  const float qk_scale = a.qk_scale;
+
+  auto load_tile = [&](int j, uint4 (&kr)[NL], uint4 (&vr)[NL]) {
+    const int phys = __builtin_amdgcn_readfirstlane(s_blocks[j]);
+    const int64_t off = (int64_t)phys * blk_stride;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) kr[i] = *reinterpret_cast<const uint4*>(kbase + off + i * 1024);
+#pragma unroll
+    for (int i = 0; i < NL; ++i) vr[i] = *reinterpret_cast<const uint4*>(vbase + off + i * 1024);
+  };
+
+  auto process = [&](int j, const uint4 (&kr)[NL], const uint4 (&vr)[NL]) {
+    float sc[GT][NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i)
+#pragma unroll
+      for (int g = 0; g < GT; ++g) sc[g][i] = group_sum<LPR>(dot_chunk<QK, CK>(qf[g], kr[i])) * qk_scale;
+    float vf[NL][E];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) v_to_float<CK>(vr[i], vf[i]);
+    const int tok0 = (blk0 + j) * 16;
+    if (tok0 + 16 > ctx) {  // last, partial block of the sequence
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        const bool ok = tok0 + i * RPL + row < ctx;
+#pragma unroll
+        for (int g = 0; g < GT; ++g) sc[g][i] = ok ? sc[g][i] : kNegInf;
+#pragma unroll
+        for (int e = 0; e < E; ++e) vf[i][e] = ok ? vf[i][e] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+      float bm = sc[g][0];
+#pragma unroll
+      for (int i = 1; i < NL; ++i) bm = fmaxf(bm, sc[g][i]);
+      const float mn = fmaxf(m[g], bm);
+      const float ms = (mn == kNegInf) ? 0.f : mn;
+      const float alpha = fast_exp2(m[g] - ms);
+      float p[NL];
+      float ls = 0.f;
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        p[i] = fast_exp2(sc[g][i] - ms);
+        ls += p[i];
+      }
+      l[g] = l[g] * alpha + ls;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        float t = acc[g][e] * alpha;
+#pragma unroll
+        for (int i = 0; i < NL; ++i) t = __builtin_fmaf(p[i], vf[i][e], t);
+        acc[g][e] = t;
+      }
+      m[g] = mn;
+    }
+  };
+
+  {
+    uint4 k0[NL], v0[NL], k1[NL], v1[NL];
+    int j = wave;
+    if (j < nblk) load_tile(j, k0, v0);
+    for (; j < nblk; j += 2 * kWaves) {
+      const int j1 = j + kWaves;
+      if (j1 < nblk) load_tile(j1, k1, v1);
+      process(j, k0, v0);
+      const int j2 = j1 + kWaves;
+      if (j2 < nblk) load_tile(j2, k0, v0);
+      if (j1 < nblk) process(j1, k1, v1);
+    }
+  }
+
+  // Merge the RPL lane groups of this wave (they saw disjoint tokens).
+#pragma unroll
+  for (int g = 0; g < GT; ++g) {
+    float mw = m[g];
+#pragma unroll
+    for (int off = LPR; off < 64; off <<= 1) mw = fmaxf(mw, __shfl_xor(mw, off, 64));
+    const float f = fast_exp2(m[g] - ((mw == kNegInf) ? 0.f : mw));
+    float lw = l[g] * f;
+#pragma unroll
+    for (int off = LPR; off < 64; off <<= 1) lw += __shfl_xor(lw, off, 64);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      float t = acc[g][e] * f;
+#pragma unroll
+      for (int off = LPR; off < 64; off <<= 1) t += __shfl_xor(t, off, 64);
+      acc[g][e] = t;
+    }
+    m[g] = mw;
+    l[g] = lw;
+  }
+  if (row == 0) {
+#pragma unroll
+    for (int g = 0; g < GT; ++g)
+#pragma unroll
+      for (int e = 0; e < E; ++e) s_acc[wave][g][col * E + e] = acc[g][e];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+      s_ml[wave][g][0] = m[g];
+      s_ml[wave][g][1] = l[g];
+    }
+  }
+  __syncthreads();
+
+  // Merge the waves; the partition holds at least one token, so M is finite.
+  for (int idx = tid; idx < GT * D; idx += kThreads) {
+    const int g = idx / D;
+    const int d = idx - g * D;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_ml[w][g][0]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float f = fast_exp2(s_ml[w][g][0] - M);
+      L += s_ml[w][g][1] * f;
+      O += s_acc[w][g][d] * f;
+    }
+    O *= a.out_scale;
+    const int64_t sh = (int64_t)seq * a.num_heads + h0 + g;
+    if (seq_parts == 1) {
+      store_out(a, sh * D + d, O / L);
+    } else {
+      const int64_t pi = sh * a.num_parts + part;
+      a.ws_out[pi * D + d] = O;
+      if (d == 0) {
+        a.ws_ml[2 * pi] = M;
+        a.ws_ml[2 * pi + 1] = L;
+      }
+    }
+  }
+}
+
+// Merge the partitions of every (sequence, head) whose context spans several.
+template <int D>
+__global__ __launch_bounds__(64) void decode_reduce(const DecodeArgs a) {
+  const int h = blockIdx.x;
+  const int seq = blockIdx.y;
+  const int lane = threadIdx.x;
+  const int ctx = a.context_lens[seq];
+  const int seq_parts = (((ctx + 15) >> 4) + a.partition_blocks - 1) / a.partition_blocks;
+  if (seq_parts <= 1) return;  // written directly by decode_main
+  const int64_t base = ((int64_t)seq * a.num_heads + h) * a.num_parts;
+  const float* ml = a.ws_ml + 2 * base;
+  const float* o = a.ws_out + base * D;
+  float M = kNegInf;
+  for (int p = 0; p < seq_parts; ++p) M = fmaxf(M, ml[2 * p]);
+  float L = 0.f;
+  float O[D / 64];
+#pragma unroll
+  for (int k = 0; k < D / 64; ++k) O[k] = 0.f;
+  for (int p = 0; p < seq_parts; ++p) {
+    const float f = fast_exp2(ml[2 * p] - M);
+    L += ml[2 * p + 1] * f;
+#pragma unroll
+    for (int k = 0; k < D / 64; ++k) O[k] += o[(int64_t)p * D + lane + 64 * k] * f;
+  }
+  const int64_t sh = (int64_t)seq * a.num_heads + h;
+#pragma unroll
+  for (int k = 0; k < D / 64; ++k) store_out(a, sh * D + lane + 64 * k, O[k] / L);
+}
+
+template <int QK, int CK, int D, int GT>
+hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
+  const dim3 grid((unsigned)(a.num_kv_heads * (a.group / GT)), (unsigned)a.num_parts, (unsigned)a.num_seqs);
+  decode_main<QK, CK, D, GT><<<grid, dim3(kThreads), 0, stream>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.num_parts == 1) return e;
+  decode_reduce<D><<<dim3((unsigned)a.num_heads, (unsigned)a.num_seqs), dim3(64), 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+template <int QK, int CK, int D>
+hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
+  switch (a.group_tile) {
+    case 1: return launch_t<QK, CK, D, 1>(a, stream);
+    case 2: return launch_t<QK, CK, D, 2>(a, stream);
+    case 4: return launch_t<QK, CK, D, 4>(a, stream);
+    case 8: return launch_t<QK, CK, D, 8>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int QK, int CK>
+hipError_t launch_d(const DecodeArgs& a, hipStream_t stream) {
+  switch (a.head_size) {
+    case 64: return launch_g<QK, CK, 64>(a, stream);
+    case 128: return launch_g<QK, CK, 128>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a, int q_kind, int cache_kind, hipStream_t stream) {
+  switch (q_kind * 4 + cache_kind) {
+    case kF32 * 4 + kF32: return launch_d<kF32, kF32>(a, stream);
+    case kF16 * 4 + kF16: return launch_d<kF16, kF16>(a, stream);
+    case kBF16 * 4 + kBF16: return launch_d<kBF16, kBF16>(a, stream);
+    case kF16 * 4 + kFP8: return launch_d<kF16, kFP8>(a, stream);
+    case kBF16 * 4 + kFP8: return launch_d<kBF16, kFP8>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace pa

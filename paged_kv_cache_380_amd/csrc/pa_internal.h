@@ -1,0 +1,61 @@
+// Host-side declarations shared by the C-ABI layer and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+struct ReshapeArgs {
+  const void* key;
+  const void* value;
+  void* k_cache;
+  void* v_cache;
+  const void* slots;
+  int64_t num_tokens;
+  int num_kv_heads;
+  int head_size;
+  int slot_is_int64;
+  float k_scale;
+  float v_scale;
+};
+
+// Returns a hipError_t of the launch.
+hipError_t launch_reshape(const ReshapeArgs& a, int src_kind, int cache_kind, hipStream_t stream);
+
+struct DecodeArgs {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  float* ws_out;          // [S, H, P, D] unnormalised partition outputs
+  float* ws_ml;           // [S, H, P, 2] partition max (log2 domain) and sum
+  float qk_scale;         // scale * log2(e) (* k_scale for FP8 caches)
+  float out_scale;        // v_scale for FP8 caches, else 1
+  int num_seqs;
+  int num_heads;
+  int num_kv_heads;
+  int head_size;
+  int group;              // num_heads / num_kv_heads
+  int group_tile;         // query heads handled by one workgroup (divides group)
+  int max_blocks;         // block table row length
+  int partition_blocks;   // blocks per partition
+  int num_parts;          // ceil(max_blocks / partition_blocks)
+  int out_kind;           // Kind of out: F32 or the query kind
+};
+
+hipError_t launch_decode(const DecodeArgs& a, int q_kind, int cache_kind, hipStream_t stream);
+
+// Largest query-head tile (8, 4, 2 or 1) dividing the group size.
+inline int group_tile_for(int group) {
+  for (int t = 8; t > 1; t /= 2)
+    if (group % t == 0) return t;
+  return 1;
+}
+
+constexpr int kMaxPartitionBlocks = 512;
+
+}  // namespace pa
