@@ -33,6 +33,7 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
+constexpr int kDepth = 2;  // blocks per wave whose K/V tiles are loaded ahead, plus the one in use
 constexpr float kNegInf = -__builtin_huge_valf();
 
 template <int QK, int CK, int D> struct QFrag {
@@ -102,6 +103,73 @@ __device__ __forceinline__ void v_to_float(const uint4& v, float* f) {
   }
 }
 
+// One lane's K chunk as packed 16-bit pairs of the query's type: FP8 codes are
+// widened exactly (scale 1) once, so every query head reuses the conversion.
+template <int QK, int CK> constexpr int kKWords = (CK == kFP8) ? 8 : 4;
+
+template <int QK, int CK>
+__device__ __forceinline__ void k_words(const uint4& k, uint32_t* w) {
+  const uint32_t kw[4] = {k.x, k.y, k.z, k.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (CK == kFP8) {
+      if constexpr (QK == kBF16) {
+        w[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)kw[i], 1.0f, false));
+        w[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)kw[i], 1.0f, true));
+      } else {
+        w[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)kw[i], 1.0f, false));
+        w[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)kw[i], 1.0f, true));
+      }
+    } else {
+      w[i] = kw[i];
+    }
+  }
+}
+
+template <int QK, int N>
+__device__ __forceinline__ float dot_words(const uint32_t* q, const uint32_t* k) {
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    if constexpr (QK == kBF16)
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, q[i]), __builtin_bit_cast(bf162_t, k[i]), acc,
+                                            false);
+    else
+      acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, q[i]), __builtin_bit_cast(half2_t, k[i]), acc, false);
+  }
+  return acc;
+}
+
+// Transposing pair sums across the two 32-lane halves (v_permlane32_swap) and
+// across 16-lane rows (v_permlane16_swap): lanes whose bit is 0 end with
+// a(own) + a(partner), lanes whose bit is 1 with b(partner) + b(own).
+__device__ __forceinline__ float swap_sum32(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float swap_sum16(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+constexpr int kDppRowRor8 = 0x128;  // lane j <- lane (j - 8) mod 16, i.e. j ^ 8
+constexpr int kDppRowRor4 = 0x124;  // lane j <- lane (j - 4) mod 16
+
+// Orders LDS traffic between lanes of one wave: the LDS executes one wave's
+// instructions in order, so only the compiler has to be kept from moving them.
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// K/V tiles are read once per step: nontemporal loads keep them from
+// displacing reusable lines in the caches.
+__device__ __forceinline__ uint4 load_stream(const char* p) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ void store_out(const DecodeArgs& a, int64_t elem, float x) {
   if (a.out_kind == kF32) {
     static_cast<float*>(a.out)[elem] = x;
@@ -109,6 +177,41 @@ __device__ __forceinline__ void store_out(const DecodeArgs& a, int64_t elem, flo
     static_cast<uint16_t*>(a.out)[elem] = f32_to_bf16_rne(x);
   } else {
     static_cast<uint16_t*>(a.out)[elem] = f32_to_f16_rne(x);
+  }
+}
+
+// Merge the waves of a workgroup (each left its max, sum and unnormalised
+// output in LDS) and write the result, or the partition's partial result.
+// The partition holds at least one token, so the merged max is finite.
+template <int GT, int D>
+__device__ __forceinline__ void finish_partition(const DecodeArgs& a, const float (&s_acc)[kWaves][GT][D],
+                                                 const float (&s_ml)[kWaves][GT][2], int seq, int h0, int part,
+                                                 int seq_parts, int tid) {
+  for (int idx = tid; idx < GT * D; idx += kThreads) {
+    const int g = idx / D;
+    const int d = idx - g * D;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_ml[w][g][0]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float f = fast_exp2(s_ml[w][g][0] - M);
+      L += s_ml[w][g][1] * f;
+      O += s_acc[w][g][d] * f;
+    }
+    O *= a.out_scale;
+    const int64_t sh = (int64_t)seq * a.num_heads + h0 + g;
+    if (seq_parts == 1) {
+      store_out(a, sh * D + d, O / L);
+    } else {
+      const int64_t pi = sh * a.num_parts + part;
+      a.ws_out[pi * D + d] = O;
+      if (d == 0) {
+        a.ws_ml[2 * pi] = M;
+        a.ws_ml[2 * pi + 1] = L;
+      }
+    }
   }
 }
 
@@ -180,38 +283,52 @@ __global__ __launch_bounds__(kThreads) void decode_main(const DecodeArgs a) {
   }
 
   const int64_t blk_stride = (int64_t)a.num_kv_heads * kTileBytes;
-  const char* kbase = static_cast<const char*>(a.k_cache) + (int64_t)kvh * kTileBytes + lane * 16;
-  const char* vbase = static_cast<const char*>(a.v_cache) + (int64_t)kvh * kTileBytes + lane * 16;
+  const char* kbase = static_cast<const char*>(a.k_cache) + (int64_t)kvh * kTileBytes;
+  const char* vbase = static_cast<const char*>(a.v_cache) + (int64_t)kvh * kTileBytes;
+  const int lane_off = lane * 16;
   const float qk_scale = a.qk_scale;
 
+  // The tile address is wave-uniform (scalar registers); each lane adds its
+  // 16-byte offset, so the loads take the scalar-base + vector-offset form.
   auto load_tile = [&](int j, uint4 (&kr)[NL], uint4 (&vr)[NL]) {
     const int phys = __builtin_amdgcn_readfirstlane(s_blocks[j]);
     const int64_t off = (int64_t)phys * blk_stride;
+    const char* kt = kbase + off;
+    const char* vt = vbase + off;
 #pragma unroll
-    for (int i = 0; i < NL; ++i) kr[i] = *reinterpret_cast<const uint4*>(kbase + off + i * 1024);
+    for (int i = 0; i < NL; ++i) kr[i] = load_stream(kt + lane_off + i * 1024);
 #pragma unroll
-    for (int i = 0; i < NL; ++i) vr[i] = *reinterpret_cast<const uint4*>(vbase + off + i * 1024);
+    for (int i = 0; i < NL; ++i) vr[i] = load_stream(vt + lane_off + i * 1024);
   };
 
-  auto process = [&](int j, const uint4 (&kr)[NL], const uint4 (&vr)[NL]) {
+  auto process = [&](int j, const uint4 (&kr)[NL], const uint4 (&vin)[NL]) {
     float sc[GT][NL];
 #pragma unroll
     for (int i = 0; i < NL; ++i)
 #pragma unroll
       for (int g = 0; g < GT; ++g) sc[g][i] = group_sum<LPR>(dot_chunk<QK, CK>(qf[g], kr[i])) * qk_scale;
-    float vf[NL][E];
+    uint4 vr[NL];
 #pragma unroll
-    for (int i = 0; i < NL; ++i) v_to_float<CK>(vr[i], vf[i]);
+    for (int i = 0; i < NL; ++i) vr[i] = vin[i];
     const int tok0 = (blk0 + j) * 16;
-    if (tok0 + 16 > ctx) {  // last, partial block of the sequence
+    if (tok0 + 16 > ctx) {  // last, partial block: drop rows past the context
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
         const bool ok = tok0 + i * RPL + row < ctx;
 #pragma unroll
         for (int g = 0; g < GT; ++g) sc[g][i] = ok ? sc[g][i] : kNegInf;
-#pragma unroll
-        for (int e = 0; e < E; ++e) vf[i][e] = ok ? vf[i][e] : 0.f;
+        vr[i].x = ok ? vr[i].x : 0u;  // all-zero bits are +0.0 in every storage type
+        vr[i].y = ok ? vr[i].y : 0u;
+        vr[i].z = ok ? vr[i].z : 0u;
+        vr[i].w = ok ? vr[i].w : 0u;
       }
+    }
+    // With one query head the V elements are widened where they are used;
+    // with several they are widened once and shared by all heads.
+    float vf[GT == 1 ? 1 : NL][E];
+    if constexpr (GT > 1) {
+#pragma unroll
+      for (int i = 0; i < NL; ++i) v_to_float<CK>(vr[i], vf[i]);
     }
 #pragma unroll
     for (int g = 0; g < GT; ++g) {
@@ -230,27 +347,37 @@ __global__ __launch_bounds__(kThreads) void decode_main(const DecodeArgs a) {
       }
       l[g] = l[g] * alpha + ls;
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        float t = acc[g][e] * alpha;
+      for (int e = 0; e < E; ++e) acc[g][e] *= alpha;
 #pragma unroll
-        for (int i = 0; i < NL; ++i) t = __builtin_fmaf(p[i], vf[i][e], t);
-        acc[g][e] = t;
+      for (int i = 0; i < NL; ++i) {
+        if constexpr (GT == 1) {
+          float f[E];
+          v_to_float<CK>(vr[i], f);
+#pragma unroll
+          for (int e = 0; e < E; ++e) acc[g][e] = __builtin_fmaf(p[i], f[e], acc[g][e]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < E; ++e) acc[g][e] = __builtin_fmaf(p[i], vf[i][e], acc[g][e]);
+        }
       }
       m[g] = mn;
     }
   };
 
   {
-    uint4 k0[NL], v0[NL], k1[NL], v1[NL];
-    int j = wave;
-    if (j < nblk) load_tile(j, k0, v0);
-    for (; j < nblk; j += 2 * kWaves) {
-      const int j1 = j + kWaves;
-      if (j1 < nblk) load_tile(j1, k1, v1);
-      process(j, k0, v0);
-      const int j2 = j1 + kWaves;
-      if (j2 < nblk) load_tile(j2, k0, v0);
-      if (j1 < nblk) process(j1, k1, v1);
+    // Ring of kDepth register buffers: the tiles of the next kDepth-1 blocks
+    // of this wave are in flight while the current one is consumed.
+    uint4 kb[kDepth][NL], vb[kDepth][NL];
+#pragma unroll
+    for (int d = 0; d < kDepth - 1; ++d)
+      if (wave + d * kWaves < nblk) load_tile(wave + d * kWaves, kb[d], vb[d]);
+    for (int j = wave; j < nblk; j += kDepth * kWaves) {
+#pragma unroll
+      for (int d = 0; d < kDepth; ++d) {
+        const int jn = j + (d + kDepth - 1) * kWaves;
+        if (jn < nblk) load_tile(jn, kb[(d + kDepth - 1) % kDepth], vb[(d + kDepth - 1) % kDepth]);
+        if (j + d * kWaves < nblk) process(j + d * kWaves, kb[d], vb[d]);
+      }
     }
   }
 
@@ -289,33 +416,264 @@ __global__ __launch_bounds__(kThreads) void decode_main(const DecodeArgs a) {
   }
   __syncthreads();
 
-  // Merge the waves; the partition holds at least one token, so M is finite.
-  for (int idx = tid; idx < GT * D; idx += kThreads) {
-    const int g = idx / D;
-    const int d = idx - g * D;
-    float M = kNegInf;
+  finish_partition<GT, D>(a, s_acc, s_ml, seq, h0, part, seq_parts, tid);
+}
+
+// Grouped-query decode for tiles of 4 or 8 query heads with 16-bit queries.
+//
+// Lane l holds 16 bytes of row r = l % RPL of every wave-load (rows i*RPL + r),
+// at column slice c = l / RPL, so the LPR lanes sharing a row are spread over
+// the high lane bits. The GT*NL partial q·k sums of a lane are reduced over
+// those bits with two transposing swap steps (bits 5 and 4), which leave each
+// lane the sums of GT/4 heads, and DPP rotations for the remaining bits. The
+// online softmax then runs once per (row, head) instead of once per lane, with
+// the running max moved only when a block's max exceeds it by more than
+// kRescaleSlack (weights stay below 2^kRescaleSlack, so float32 is safe). The
+// weights reach the lanes that hold V through a small per-wave LDS buffer.
+constexpr float kRescaleSlack = 8.0f;
+
+template <int QK, int CK, int D, int GT>
+__global__ __launch_bounds__(kThreads) void decode_gqa(const DecodeArgs a) {
+  using Geo = TileGeo<CK, D>;
+  constexpr int E = Geo::E, RPL = Geo::RPL, NL = Geo::NL;
+  constexpr int KW = kKWords<QK, CK>;  // q/K words per lane-load (16-bit pairs)
+  constexpr int kRowBits = RPL == 4 ? 2 : RPL == 8 ? 3 : 4;
+  constexpr int V0 = GT * NL;          // partial sums per lane per block
+  constexpr int HL = GT / 4;           // heads per lane after the swaps
+  constexpr int kQBytes = 2;
+  constexpr int kTileBytes = 16 * D * Geo::kBytes;
+  static_assert(GT == 4 || GT == 8, "GQA tile of 4 or 8 heads");
+  static_assert(QK == kF16 || QK == kBF16, "16-bit queries");
+  static_assert(KW * 2 == E, "q slice matches the K slice");
+
+  __shared__ int s_blocks[kMaxPartitionBlocks];
+  __shared__ float s_p[kWaves][RPL][NL][GT];
+  __shared__ float s_alpha[kWaves][RPL][GT];
+  __shared__ float s_rowml[kWaves][RPL][GT][2];
+  __shared__ float s_acc[kWaves][GT][D];
+  __shared__ float s_ml[kWaves][GT][2];
+
+  const int n_sub = a.group / GT;
+  const int kvh = blockIdx.x / n_sub;
+  const int h0 = kvh * a.group + (blockIdx.x - kvh * n_sub) * GT;
+  const int part = blockIdx.y;
+  const int seq = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+
+  const int ctx = a.context_lens[seq];
+  if (ctx <= 0) {
+    if (part == 0)
+      for (int idx = tid; idx < GT * D; idx += kThreads)
+        store_out(a, ((int64_t)seq * a.num_heads + h0) * D + idx, 0.f);
+    return;
+  }
+  const int seq_blocks = (ctx + 15) >> 4;
+  const int blk0 = part * a.partition_blocks;
+  if (blk0 >= seq_blocks) return;
+  const int nblk = min(a.partition_blocks, seq_blocks - blk0);
+  const int seq_parts = (seq_blocks + a.partition_blocks - 1) / a.partition_blocks;
+
+  const int32_t* bt = a.block_tables + (int64_t)seq * a.max_blocks + blk0;
+  for (int j = tid; j < nblk; j += kThreads) s_blocks[j] = bt[j];
+
+  const int r = lane & (RPL - 1);      // row of each wave-load
+  const int c = lane >> kRowBits;      // column slice
+  const int hq = lane >> 4;            // head quarter kept through the swaps
+  // One lane per (row, head quarter) publishes to LDS: the remaining column
+  // bits below bit 4 hold copies.
+  const bool writer = ((lane >> kRowBits) & ((1 << (4 - kRowBits)) - 1)) == 0;
+
+  uint32_t qf[GT][KW];
+  {
+    const char* qp = static_cast<const char*>(a.q) + (((int64_t)seq * a.num_heads + h0) * D + c * E) * kQBytes;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_ml[w][g][0]);
-    float L = 0.f, O = 0.f;
+    for (int g = 0; g < GT; ++g)
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float f = fast_exp2(s_ml[w][g][0] - M);
-      L += s_ml[w][g][1] * f;
-      O += s_acc[w][g][d] * f;
+      for (int w = 0; w < KW / 4; ++w) {
+        const uint4 v = *reinterpret_cast<const uint4*>(qp + g * D * kQBytes + w * 16);
+        qf[g][4 * w] = v.x;
+        qf[g][4 * w + 1] = v.y;
+        qf[g][4 * w + 2] = v.z;
+        qf[g][4 * w + 3] = v.w;
+      }
+  }
+  __syncthreads();
+
+  float acc[GT][E];
+#pragma unroll
+  for (int g = 0; g < GT; ++g)
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[g][e] = 0.f;
+  float mref[HL], lsum[HL];
+#pragma unroll
+  for (int jj = 0; jj < HL; ++jj) {
+    mref[jj] = kNegInf;
+    lsum[jj] = 0.f;
+  }
+
+  const int64_t blk_stride = (int64_t)a.num_kv_heads * kTileBytes;
+  const char* kbase = static_cast<const char*>(a.k_cache) + (int64_t)kvh * kTileBytes;
+  const char* vbase = static_cast<const char*>(a.v_cache) + (int64_t)kvh * kTileBytes;
+  const int lane_off = r * (D * Geo::kBytes) + c * 16;
+  const float qk_scale = a.qk_scale;
+
+  auto load_tile = [&](int j, uint4 (&kr)[NL], uint4 (&vr)[NL]) {
+    const int phys = __builtin_amdgcn_readfirstlane(s_blocks[j]);
+    const int64_t off = (int64_t)phys * blk_stride;
+    const char* kt = kbase + off;
+    const char* vt = vbase + off;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) kr[i] = load_stream(kt + lane_off + i * 1024);
+#pragma unroll
+    for (int i = 0; i < NL; ++i) vr[i] = load_stream(vt + lane_off + i * 1024);
+  };
+
+  auto process = [&](int j, const uint4 (&kr)[NL], const uint4 (&vin)[NL]) {
+    float x[V0];  // x[g*NL + i] = partial q_g . k_(i*RPL + r) over this lane's slice
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      uint32_t kw[KW];
+      k_words<QK, CK>(kr[i], kw);
+#pragma unroll
+      for (int g = 0; g < GT; ++g) x[g * NL + i] = dot_words<QK, KW>(qf[g], kw);
     }
-    O *= a.out_scale;
-    const int64_t sh = (int64_t)seq * a.num_heads + h0 + g;
-    if (seq_parts == 1) {
-      store_out(a, sh * D + d, O / L);
-    } else {
-      const int64_t pi = sh * a.num_parts + part;
-      a.ws_out[pi * D + d] = O;
-      if (d == 0) {
-        a.ws_ml[2 * pi] = M;
-        a.ws_ml[2 * pi + 1] = L;
+    float y[V0 / 2];
+#pragma unroll
+    for (int k = 0; k < V0 / 2; ++k) y[k] = swap_sum32(x[k], x[k + V0 / 2]);
+    float z[V0 / 4];  // z[jj*NL + i]: head hq*HL + jj, token i*RPL + r
+#pragma unroll
+    for (int k = 0; k < V0 / 4; ++k) {
+      float t = swap_sum16(y[k], y[k + V0 / 4]);
+      if constexpr (RPL <= 8) t += dpp<kDppRowRor8>(t);
+      if constexpr (RPL == 4) t += dpp<kDppRowRor4>(t);
+      z[k] = t * qk_scale;
+    }
+    uint4 vr[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) vr[i] = vin[i];
+    const int tok0 = (blk0 + j) * 16;
+    if (tok0 + 16 > ctx) {  // last, partial block: drop rows past the context
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        const bool ok = tok0 + i * RPL + r < ctx;
+#pragma unroll
+        for (int jj = 0; jj < HL; ++jj) z[jj * NL + i] = ok ? z[jj * NL + i] : kNegInf;
+        vr[i].x = ok ? vr[i].x : 0u;
+        vr[i].y = ok ? vr[i].y : 0u;
+        vr[i].z = ok ? vr[i].z : 0u;
+        vr[i].w = ok ? vr[i].w : 0u;
+      }
+    }
+    float bm[HL];
+    bool need = false;
+#pragma unroll
+    for (int jj = 0; jj < HL; ++jj) {
+      bm[jj] = z[jj * NL];
+#pragma unroll
+      for (int i = 1; i < NL; ++i) bm[jj] = fmaxf(bm[jj], z[jj * NL + i]);
+      need |= bm[jj] > mref[jj] + kRescaleSlack;
+    }
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {  // move the reference max (wave-uniform branch)
+#pragma unroll
+      for (int jj = 0; jj < HL; ++jj) {
+        const float mn = fmaxf(mref[jj], bm[jj]);
+        const float al = fast_exp2(mref[jj] - ((mn == kNegInf) ? 0.f : mn));
+        lsum[jj] *= al;
+        mref[jj] = mn;
+        if (writer) s_alpha[wave][r][hq * HL + jj] = al;
+      }
+      wave_lds_fence();
+#pragma unroll
+      for (int g = 0; g < GT; ++g) {
+        const float al = s_alpha[wave][r][g];
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[g][e] *= al;
+      }
+    }
+#pragma unroll
+    for (int jj = 0; jj < HL; ++jj) {
+      const float ms = (mref[jj] == kNegInf) ? 0.f : mref[jj];
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        const float pv = fast_exp2(z[jj * NL + i] - ms);
+        lsum[jj] += pv;
+        if (writer) s_p[wave][r][i][hq * HL + jj] = pv;
+      }
+    }
+    wave_lds_fence();
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      float vf[E];
+      v_to_float<CK>(vr[i], vf);
+      float pg[GT];
+#pragma unroll
+      for (int g = 0; g < GT; ++g) pg[g] = s_p[wave][r][i][g];
+#pragma unroll
+      for (int g = 0; g < GT; ++g)
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[g][e] = __builtin_fmaf(pg[g], vf[e], acc[g][e]);
+    }
+  };
+
+  {
+    uint4 kb[kDepth][NL], vb[kDepth][NL];
+#pragma unroll
+    for (int d = 0; d < kDepth - 1; ++d)
+      if (wave + d * kWaves < nblk) load_tile(wave + d * kWaves, kb[d], vb[d]);
+    for (int j = wave; j < nblk; j += kDepth * kWaves) {
+#pragma unroll
+      for (int d = 0; d < kDepth; ++d) {
+        const int jn = j + (d + kDepth - 1) * kWaves;
+        if (jn < nblk) load_tile(jn, kb[(d + kDepth - 1) % kDepth], vb[(d + kDepth - 1) % kDepth]);
+        if (j + d * kWaves < nblk) process(j + d * kWaves, kb[d], vb[d]);
       }
     }
   }
+
+  // Merge the RPL rows of this wave: publish each (row, head) max and sum,
+  // rescale the accumulators to the wave's max, then sum over the row lanes.
+  if (writer) {
+#pragma unroll
+    for (int jj = 0; jj < HL; ++jj) {
+      s_rowml[wave][r][hq * HL + jj][0] = mref[jj];
+      s_rowml[wave][r][hq * HL + jj][1] = lsum[jj];
+    }
+  }
+  wave_lds_fence();
+#pragma unroll
+  for (int g = 0; g < GT; ++g) {
+    float mw = kNegInf;
+#pragma unroll
+    for (int rr = 0; rr < RPL; ++rr) mw = fmaxf(mw, s_rowml[wave][rr][g][0]);
+    const float mws = (mw == kNegInf) ? 0.f : mw;
+    const float f = fast_exp2(s_rowml[wave][r][g][0] - mws);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      float t = acc[g][e] * f;
+      t += dpp<kDppQuadXor1>(t);
+      t += dpp<kDppQuadXor2>(t);
+      if constexpr (RPL >= 8) t += dpp<kDppRowHalfMirror>(t);
+      if constexpr (RPL >= 16) t += dpp<kDppRowMirror>(t);
+      acc[g][e] = t;
+    }
+    if (lane == 0) {
+      float lw = 0.f;
+#pragma unroll
+      for (int rr = 0; rr < RPL; ++rr) lw += s_rowml[wave][rr][g][1] * fast_exp2(s_rowml[wave][rr][g][0] - mws);
+      s_ml[wave][g][0] = mw;
+      s_ml[wave][g][1] = lw;
+    }
+  }
+  if (r == 0) {
+#pragma unroll
+    for (int g = 0; g < GT; ++g)
+#pragma unroll
+      for (int e = 0; e < E; ++e) s_acc[wave][g][c * E + e] = acc[g][e];
+  }
+  __syncthreads();
+  finish_partition<GT, D>(a, s_acc, s_ml, seq, h0, part, seq_parts, tid);
 }
 
 // Merge the partitions of every (sequence, head) whose context spans several.
@@ -350,7 +708,10 @@ __global__ __launch_bounds__(64) void decode_reduce(const DecodeArgs a) {
 template <int QK, int CK, int D, int GT>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)(a.num_kv_heads * (a.group / GT)), (unsigned)a.num_parts, (unsigned)a.num_seqs);
-  decode_main<QK, CK, D, GT><<<grid, dim3(kThreads), 0, stream>>>(a);
+  if constexpr (GT >= 4 && QK != kF32)
+    decode_gqa<QK, CK, D, GT><<<grid, dim3(kThreads), 0, stream>>>(a);
+  else
+    decode_main<QK, CK, D, GT><<<grid, dim3(kThreads), 0, stream>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.num_parts == 1) return e;
   decode_reduce<D><<<dim3((unsigned)a.num_heads, (unsigned)a.num_seqs), dim3(64), 0, stream>>>(a);
