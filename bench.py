@@ -46,7 +46,7 @@ def kernel_source_sha() -> str:
 
 def counter_traffic(workload: str, algorithmic_bytes: float):
     """HBM bytes per decode launch from the committed rocprofv3 counter summary, if it is current."""
-    path = os.path.join(PROFILES, f"decode_main_{workload}_counters.txt")
+    path = os.path.join(PROFILES, f"decode_{workload}_counters.txt")
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -58,6 +58,98 @@ def counter_traffic(workload: str, algorithmic_bytes: float):
         return None  # the kernel changed since the counters were taken
     b = field("hbm_bytes_per_dispatch")
     return b
+
+
+def decode_algorithmic_bytes(w) -> int:
+    """Bytes one decode launch must move: each K/V tile once (shared-prefix tiles once), q, out, table, lengths."""
+    from paged_kv_cache_380_amd import workloads as wl
+    act = wl.TORCH_DTYPES[w.dtype].itemsize
+    return (wl.algorithmic_kv_bytes(w, unique=True) + 2 * w.num_seqs * w.num_heads * w.head_size * act
+            + w.block_tables.numel() * 4 + w.num_seqs * 4)
+
+
+# --- rocprofv3 summaries (run on the host, over the CSV files a profiled run left) -------------
+
+def _csv_rows(directory: str, suffix: str):
+    import csv
+    import glob
+    rows = []
+    for path in sorted(glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True)):
+        with open(path, newline="") as f:
+            rows.extend(csv.DictReader(f))
+    if not rows:
+        raise SystemExit(f"no *{suffix} under {directory}")
+    return rows
+
+
+def _col(row: dict, *names):
+    low = {k.lower(): v for k, v in row.items()}
+    for n in names:
+        if n.lower() in low:
+            return low[n.lower()]
+    raise KeyError(f"none of {names} in {list(row)}")
+
+
+def _short(name: str) -> str:
+    m = re.search(r"([A-Za-z_][A-Za-z0-9_]*)(<[^()]*>)?\(", name)
+    return (m.group(1) + (m.group(2) or "")) if m else name[:80]
+
+
+def summarize_stats(directory: str, out_path: str, command: str):
+    rows = _csv_rows(directory, "kernel_stats.csv")
+    lines = [f"# rocprofv3 kernel statistics", f"command: {command}", "",
+             f"{'kernel':<60} {'calls':>7} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}"]
+    for r in sorted(rows, key=lambda r: -float(_col(r, "TotalDurationNs"))):
+        lines.append(f"{_short(_col(r, 'Name')):<60} {int(_col(r, 'Calls')):>7} "
+                     f"{float(_col(r, 'AverageNs')) / 1e3:>10.2f} {float(_col(r, 'MinNs')) / 1e3:>10.2f} "
+                     f"{float(_col(r, 'MaxNs')) / 1e3:>10.2f} {float(_col(r, 'Percentage')):>6.2f}")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def _counter_means(directory: str, counter: str, select) -> tuple[float, int, str]:
+    vals, names = {}, set()
+    for r in _csv_rows(directory, "counter_collection.csv"):
+        name = _col(r, "Kernel_Name")
+        if _col(r, "Counter_Name") != counter or not select(name):
+            continue
+        key = _col(r, "Dispatch_Id", "Correlation_Id")
+        vals[key] = vals.get(key, 0.0) + float(_col(r, "Counter_Value"))
+        names.add(_short(name))
+    if not vals:
+        raise SystemExit(f"no {counter} rows for the selected kernel under {directory}")
+    return sum(vals.values()) / len(vals), len(vals), ", ".join(sorted(names))
+
+
+def summarize_counters(workload: str, fetch_dir: str, write_dir: str, cal_fetch_dir: str, cal_write_dir: str,
+                       copy_mib: int, out_path: str, commands: list[str]):
+    """HBM bytes per decode launch: FETCH_SIZE and WRITE_SIZE (KiB) scaled by what they read for a plain copy."""
+    from paged_kv_cache_380_amd import workloads as wl
+    is_decode = lambda n: "decode_main" in n or "decode_gqa" in n
+    is_copy = lambda n: "copy" in n.lower()
+    fetch, nf, kname = _counter_means(fetch_dir, "FETCH_SIZE", is_decode)
+    write, nw, _ = _counter_means(write_dir, "WRITE_SIZE", is_decode)
+    cfetch, _, cname = _counter_means(cal_fetch_dir, "FETCH_SIZE", is_copy)
+    cwrite, _, _ = _counter_means(cal_write_dir, "WRITE_SIZE", is_copy)
+    copy_bytes = copy_mib << 20
+    ff, fw = copy_bytes / (cfetch * 1024), copy_bytes / (cwrite * 1024)
+    hbm = ff * fetch * 1024 + fw * write * 1024
+    w = wl.named(workload)
+    algo = decode_algorithmic_bytes(w)
+    lines = [
+        "# rocprofv3 HBM counters of the decode kernel",
+        f"workload: {w.name}", f"kernel: {kname}", f"kernel_source_sha: {kernel_source_sha()}",
+        f"dispatches: {nf} (FETCH_SIZE run), {nw} (WRITE_SIZE run)",
+        f"FETCH_SIZE_KiB_per_dispatch: {fetch:.1f}", f"WRITE_SIZE_KiB_per_dispatch: {write:.1f}",
+        f"calibration_kernel: {cname} ({copy_mib} MiB read + {copy_mib} MiB written)",
+        f"calibration_FETCH_SIZE_KiB: {cfetch:.1f}", f"calibration_WRITE_SIZE_KiB: {cwrite:.1f}",
+        f"fetch_factor: {ff:.4f}", f"write_factor: {fw:.4f}",
+        f"hbm_bytes_per_dispatch: {hbm:.0f}", f"algorithmic_bytes_per_dispatch: {algo}",
+        f"traffic_over_algorithmic: {hbm / algo:.4f}", "commands:"] + [f"  {c}" for c in commands]
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def cpu_baseline(w, target_seconds: float):
@@ -77,15 +169,21 @@ def cpu_baseline(w, target_seconds: float):
     per_tok = w.num_kv_heads * w.head_size * 2 * w.kv_bytes_per_elem()
     r0 = resource.getrusage(resource.RUSAGE_SELF)
     t0 = time.perf_counter()
-    for s in order:
-        oracle.reshape_and_cache(nk[s:s + 1], nv[s:s + 1], kc, vc, ns[s:s + 1], w.block_size, w.dtype,
-                                 w.cache_dtype, w.k_scale, w.v_scale)
-        oracle.decode_attention(q, kc, vc, tables, lens, w.scale, w.num_kv_heads, w.block_size, w.dtype,
-                                w.cache_dtype, w.k_scale, w.v_scale, seqs=[int(s)])
-        done.append(int(s))
-        kv_bytes += int(lens[s]) * per_tok
-        if time.perf_counter() - t0 >= target_seconds:
-            break
+    passes = 0
+    while True:  # whole passes over the sampled order until the time bound (one sequence = one unit)
+        for s in order:
+            oracle.reshape_and_cache(nk[s:s + 1], nv[s:s + 1], kc, vc, ns[s:s + 1], w.block_size, w.dtype,
+                                     w.cache_dtype, w.k_scale, w.v_scale)
+            oracle.decode_attention(q, kc, vc, tables, lens, w.scale, w.num_kv_heads, w.block_size, w.dtype,
+                                    w.cache_dtype, w.k_scale, w.v_scale, seqs=[int(s)])
+            done.append(int(s))
+            kv_bytes += int(lens[s]) * per_tok
+            if time.perf_counter() - t0 >= target_seconds:
+                break
+        else:
+            passes += 1
+            continue
+        break
     wall = time.perf_counter() - t0
     r1 = resource.getrusage(resource.RUSAGE_SELF)
     cpu = (r1.ru_utime - r0.ru_utime) + (r1.ru_stime - r0.ru_stime)
@@ -93,7 +191,8 @@ def cpu_baseline(w, target_seconds: float):
     return {
         "value": kv_bytes / wall / 1e9, "unit": "GB/s", "cores": max(1, round(cpu / wall)),
         "kind": "oracle",
-        "sample": f"{len(done)} of {w.num_seqs} sequences (reshape of their new token + fp64 decode), "
+        "sample": f"{len(done)} sequence-steps ({passes} whole passes over the {w.num_seqs} sequences, then "
+                  f"{len(done) - passes * w.num_seqs} more; reshape of the new token + fp64 decode each), "
                   f"{wall:.1f} s wall, {cpu:.1f} s CPU, {len(os.sched_getaffinity(0))} host cores visible",
         "seq_steps_per_s": len(done) / wall,
     }
@@ -111,7 +210,21 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of this many MiB (for counter calibration) and exit")
+    ap.add_argument("--summarize-stats", nargs=3, metavar=("DIR", "OUT", "COMMAND"),
+                    help="write a kernel-statistics summary of a rocprofv3 --kernel-trace --stats run and exit")
+    ap.add_argument("--summarize-counters", nargs=6,
+                    metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR", "COPY_MIB", "OUT"),
+                    help="write the HBM-traffic summary of rocprofv3 --pmc runs for --workload and exit")
+    ap.add_argument("--command", action="append", default=[], help="profiling commands recorded in a summary")
     args = ap.parse_args()
+
+    if args.summarize_stats:
+        summarize_stats(*args.summarize_stats)
+        return
+    if args.summarize_counters:
+        fd, wd, cfd, cwd, mib, out = args.summarize_counters
+        summarize_counters(args.workload, fd, wd, cfd, cwd, int(mib), out, args.command)
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path.",
@@ -184,9 +297,7 @@ def main():
     kv_bytes = wl.algorithmic_kv_bytes(w)
     kv_unique = wl.algorithmic_kv_bytes(w, unique=True)
     step_bytes = wl.algorithmic_step_bytes(w)
-    act = torch.empty((), dtype=case.q.dtype).element_size()
-    decode_bytes = kv_unique + 2 * w.num_seqs * w.num_heads * w.head_size * act + w.block_tables.numel() * 4 \
-        + w.num_seqs * 4
+    decode_bytes = decode_algorithmic_bytes(w)
     achieved = decode_bytes / (decode_ms * 1e-3) / 1e9
     traffic = counter_traffic(w.name, decode_bytes)
 
