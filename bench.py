@@ -29,7 +29,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_380_amd", "csrc", f)
-                  for f in ("pa_decode.hip", "pa_device.h", "pa_internal.h")]
+                  for f in ("pa_decode.hip", "pa_decode_mfma.hip", "pa_decode_common.h", "pa_device.h",
+                            "pa_internal.h")]
 
 
 def log(*a):
@@ -126,7 +127,7 @@ def summarize_counters(workload: str, fetch_dir: str, write_dir: str, cal_fetch_
                        copy_mib: int, out_path: str, commands: list[str]):
     """HBM bytes per decode launch: FETCH_SIZE and WRITE_SIZE (KiB) scaled by what they read for a plain copy."""
     from paged_kv_cache_380_amd import workloads as wl
-    is_decode = lambda n: "decode_main" in n or "decode_gqa" in n
+    is_decode = lambda n: "decode_main" in n or "decode_gqa" in n or "decode_mfma" in n
     is_copy = lambda n: "copy" in n.lower()
     fetch, nf, kname = _counter_means(fetch_dir, "FETCH_SIZE", is_decode)
     write, nw, _ = _counter_means(write_dir, "WRITE_SIZE", is_decode)
@@ -319,13 +320,14 @@ def main():
             "workload": w.name, "num_seqs": w.num_seqs, "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads,
             "head_size": w.head_size, "block_size": w.block_size, "context_tokens": int(w.context_lens.sum()),
             "kv_cache_dtype": w.cache_dtype, "partition_blocks": pb, "seed": w.seed,
+            "decode_path": os.environ.get("PA_DECODE_PATH", "auto"),
         },
         "pct_of_hbm_peak": round(100 * kv_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
         "seq_steps_per_s": round(w.num_seqs / (ms_per_step * 1e-3), 1),
         "decode_ms": round(decode_ms, 5),
         "decode_ms_p10_p90": [round(durs[len(durs) // 10], 5), round(durs[(9 * len(durs)) // 10], 5)],
         "roofline": {
-            "kernel": "decode_main" + ("" if wl_parts(w, pb) == 1 else " + decode_reduce"),
+            "kernel": decode_kernel(w) + ("" if wl_parts(w, pb) == 1 else " + decode_reduce"),
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": None if traffic is None else round(traffic),
@@ -340,6 +342,17 @@ def main():
         log(f"[bench] oracle sample (~{args.cpu_seconds:.0f} s)")
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(res), flush=True)
+
+
+def decode_kernel(w) -> str:
+    """Name of the decode kernel the library runs for this workload (its selection rule, restated)."""
+    group = w.num_heads // w.num_kv_heads
+    path = os.environ.get("PA_DECODE_PATH", "auto")
+    if w.dtype in ("f16", "bf16") and group % 4 == 0 and path != "valu":
+        return "decode_mfma"
+    if w.dtype in ("f16", "bf16") and group % 4 == 0:
+        return "decode_gqa"
+    return "decode_main"
 
 
 def wl_parts(w, pb: int) -> int:

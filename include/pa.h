@@ -40,12 +40,13 @@
  * Errors: 0 (PA_OK) on success, otherwise a pa_status code, with a message
  * for the calling thread in pa_last_error(). Arguments are validated on the
  * host without reading device memory; nothing is launched when validation
- * fails. Block ids, slots and context lengths are device data and are NOT
- * checked: an id outside [0, num_blocks), a slot outside
- * [0, num_blocks*block_size) or a context length above
- * max_blocks_per_seq*block_size is undefined behaviour (a GPU memory fault).
- * Launch failures are reported as PA_ERR_LAUNCH; faults inside a kernel
- * surface at the caller's next synchronisation.
+ * fails. Block ids, slots and context lengths are device data and cannot be
+ * validated on the host; the kernels keep every access inside the caller's
+ * buffers instead: a context length above max_blocks_per_seq*block_size is
+ * treated as that maximum, a block id outside [0, num_blocks) reads block 0,
+ * and a slot at or past num_blocks*block_size is skipped like a negative one.
+ * Such inputs give meaningless results, never a memory fault. Launch
+ * failures are reported as PA_ERR_LAUNCH.
  */
 #ifndef PA_H_
 #define PA_H_
@@ -132,6 +133,13 @@ int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void
  * split: each partition writes its running max, sum and unnormalised output
  * to the workspace, and a second kernel merges the partitions in a fixed
  * order, so results are deterministic run to run.
+ *
+ * Kernel choice: with F16/BF16 queries and a multiple of 4 query heads per
+ * KV head, the products of a K/V tile with the group's queries run on the
+ * matrix cores (MFMA); otherwise on the vector ALU. Both give the result above
+ * within float32 accumulation error. The environment variable PA_DECODE_PATH
+ * (read on every call) forces "valu" or "mfma" (the latter only where it
+ * applies), for comparison runs.
  */
 int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
               const int32_t* block_tables, const int32_t* context_lens, float scale,

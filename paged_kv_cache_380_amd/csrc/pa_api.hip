@@ -4,6 +4,8 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
+#include <cstring>
 #include <string>
 
 #include "pa.h"
@@ -30,9 +32,12 @@ int ok() {
 
 bool activation_kind(int k) { return k == PA_DTYPE_F32 || k == PA_DTYPE_F16 || k == PA_DTYPE_BF16; }
 
-// Workgroups wanted before a context is split: with 256 compute units this
-// keeps every unit several workgroups deep.
-constexpr int64_t kTargetWorkgroups = 1024;
+// Workgroups wanted before a context is split: one resident round on 256
+// compute units at two workgroups each. Splitting further was measured to
+// lose more to per-workgroup start-up, partial-result traffic and the merge
+// than it gains in balance; a round of 512 long-running workgroups keeps
+// every unit streaming until the end.
+constexpr int64_t kTargetWorkgroups = 512;
 
 int choose_partition_blocks(int num_seqs, int num_heads, int num_kv_heads, int max_blocks) {
   const int group = num_heads / num_kv_heads;
@@ -44,6 +49,25 @@ int choose_partition_blocks(int num_seqs, int num_heads, int num_kv_heads, int m
   if (pb < 4) pb = 4;
   if (pb > pa::kMaxPartitionBlocks) pb = pa::kMaxPartitionBlocks;
   return (int)pb;
+}
+
+// Decode kernel family: PA_DECODE_PATH=valu or =mfma forces one (mfma only
+// where it applies); unset or anything else picks automatically. Read on every
+// call (a getenv costs far less than a launch), so a process can switch.
+enum class Path { kAuto, kValu, kMfma };
+Path requested_path() {
+  const char* e = std::getenv("PA_DECODE_PATH");
+  if (e && !std::strcmp(e, "valu")) return Path::kValu;
+  if (e && !std::strcmp(e, "mfma")) return Path::kMfma;
+  return Path::kAuto;
+}
+
+// The matrix-core kernel serves 16-bit queries whose group of query heads per
+// KV head is a multiple of 4: there one K/V tile feeds a [group x head_size]
+// product. Below that (and for float32 data) the vector-ALU kernels run.
+bool use_mfma(int q_dtype, int group) {
+  const bool applies = (q_dtype == PA_DTYPE_F16 || q_dtype == PA_DTYPE_BF16) && pa::mfma_group_tile(group) != 0;
+  return applies && requested_path() != Path::kValu;
 }
 
 bool shapes_ok(int num_seqs, int num_heads, int num_kv_heads, int head_size, int max_blocks, int block_size) {
@@ -102,7 +126,7 @@ int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void
   if (num_tokens == 0) return ok();
   if (!key || !value || !k_cache || !v_cache || !slot_mapping)
     return fail(PA_ERR_NULL, "reshape_and_cache: NULL pointer argument");
-  pa::ReshapeArgs a{key, value, k_cache, v_cache, slot_mapping, num_tokens, num_kv_heads, head_size,
+  pa::ReshapeArgs a{key, value, k_cache, v_cache, slot_mapping, num_tokens, num_blocks, num_kv_heads, head_size,
                     slot_is_int64 ? 1 : 0, k_scale, v_scale};
   const hipError_t e = pa::launch_reshape(a, kv_dtype, cache_dtype, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "reshape_and_cache: launch failed: %s", hipGetErrorString(e));
@@ -190,7 +214,9 @@ int pa_decode_split(void* out, const void* q, const void* k_cache, const void* v
   a.num_kv_heads = num_kv_heads;
   a.head_size = head_size;
   a.group = num_heads / num_kv_heads;
-  a.group_tile = pa::group_tile_for(a.group);
+  a.use_mfma = use_mfma(q_dtype, a.group) ? 1 : 0;
+  a.group_tile = a.use_mfma ? pa::mfma_group_tile(a.group) : pa::group_tile_for(a.group);
+  a.num_blocks = num_blocks;
   a.max_blocks = max_blocks_per_seq;
   a.partition_blocks = pb;
   a.num_parts = L.num_parts;

@@ -25,54 +25,67 @@
 //    them in partition order (deterministic).
 // Rows past the context (the tail of the last block) are removed by selection,
 // never by multiplying with zero, so stale or NaN data there cannot leak.
-#include "pa_device.h"
-#include "pa_internal.h"
+#include <type_traits>
+
+#include "pa_decode_common.h"
 
 namespace pa {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kDepth = 2;  // blocks per wave whose K/V tiles are loaded ahead, plus the one in use
-constexpr float kNegInf = -__builtin_huge_valf();
 
 template <int QK, int CK, int D> struct QFrag {
   static constexpr int kElems = TileGeo<CK, D>::E;                     // q elements per lane
   static constexpr int kWords = (QK == kF32) ? kElems : kElems / 2;    // 32-bit words per lane
 };
 
+// First term of a packed 16-bit dot product: the VOP3 form with an inline
+// zero addend, so the accumulator needs no zeroing move (the compiler would
+// otherwise pick the tied-accumulator form and zero a register first).
+template <int QK>
+__device__ __forceinline__ float dot2_first(uint32_t a, uint32_t b) {
+  float r;
+  if constexpr (QK == kBF16)
+    asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+  else
+    asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
+template <int QK>
+__device__ __forceinline__ float dot2_acc(uint32_t a, uint32_t b, float acc) {
+  if constexpr (QK == kBF16)
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, a), __builtin_bit_cast(bf162_t, b), acc, false);
+  else
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), acc, false);
+}
+
 // Partial q·k over the E elements one lane holds of a token row.
 template <int QK, int CK>
 __device__ __forceinline__ float dot_chunk(const uint32_t* qw, const uint4& k) {
   const uint32_t kw[4] = {k.x, k.y, k.z, k.w};
-  float acc = 0.f;
+  float acc;
   if constexpr (CK == kF32) {
+    acc = __uint_as_float(qw[0]) * __uint_as_float(kw[0]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc = __builtin_fmaf(__uint_as_float(qw[i]), __uint_as_float(kw[i]), acc);
-  } else if constexpr (CK == kF16) {
+    for (int i = 1; i < 4; ++i) acc = __builtin_fmaf(__uint_as_float(qw[i]), __uint_as_float(kw[i]), acc);
+  } else if constexpr (CK == kF16 || CK == kBF16) {
+    acc = dot2_first<CK>(qw[0], kw[0]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, qw[i]), __builtin_bit_cast(half2_t, kw[i]), acc, false);
-  } else if constexpr (CK == kBF16) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, qw[i]), __builtin_bit_cast(bf162_t, kw[i]),
-                                            acc, false);
+    for (int i = 1; i < 4; ++i) acc = dot2_acc<CK>(qw[i], kw[i], acc);
   } else {
     // FP8 codes widen exactly to the query's 16-bit type (scale 1), then dot2.
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+      uint32_t lo, hi;
       if constexpr (QK == kBF16) {
-        const bf162_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)kw[i], 1.0f, false);
-        const bf162_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)kw[i], 1.0f, true);
-        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, qw[2 * i]), lo, acc, false);
-        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, qw[2 * i + 1]), hi, acc, false);
+        lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)kw[i], 1.0f, false));
+        hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)kw[i], 1.0f, true));
       } else {
-        const half2_t lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)kw[i], 1.0f, false);
-        const half2_t hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)kw[i], 1.0f, true);
-        acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, qw[2 * i]), lo, acc, false);
-        acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, qw[2 * i + 1]), hi, acc, false);
+        lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)kw[i], 1.0f, false));
+        hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)kw[i], 1.0f, true));
       }
+      acc = (i == 0) ? dot2_first<QK>(qw[0], lo) : dot2_acc<QK>(qw[2 * i], lo, acc);
+      acc = dot2_acc<QK>(qw[2 * i + 1], hi, acc);
     }
   }
   return acc;
@@ -128,15 +141,9 @@ __device__ __forceinline__ void k_words(const uint4& k, uint32_t* w) {
 
 template <int QK, int N>
 __device__ __forceinline__ float dot_words(const uint32_t* q, const uint32_t* k) {
-  float acc = 0.f;
+  float acc = dot2_first<QK>(q[0], k[0]);
 #pragma unroll
-  for (int i = 0; i < N; ++i) {
-    if constexpr (QK == kBF16)
-      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, q[i]), __builtin_bit_cast(bf162_t, k[i]), acc,
-                                            false);
-    else
-      acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, q[i]), __builtin_bit_cast(half2_t, k[i]), acc, false);
-  }
+  for (int i = 1; i < N; ++i) acc = dot2_acc<QK>(q[i], k[i], acc);
   return acc;
 }
 
@@ -153,67 +160,6 @@ __device__ __forceinline__ float swap_sum16(float a, float b) {
 }
 constexpr int kDppRowRor8 = 0x128;  // lane j <- lane (j - 8) mod 16, i.e. j ^ 8
 constexpr int kDppRowRor4 = 0x124;  // lane j <- lane (j - 4) mod 16
-
-// Orders LDS traffic between lanes of one wave: the LDS executes one wave's
-// instructions in order, so only the compiler has to be kept from moving them.
-__device__ __forceinline__ void wave_lds_fence() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// K/V tiles are read once per step: nontemporal loads keep them from
-// displacing reusable lines in the caches.
-__device__ __forceinline__ uint4 load_stream(const char* p) {
-  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-
-__device__ __forceinline__ void store_out(const DecodeArgs& a, int64_t elem, float x) {
-  if (a.out_kind == kF32) {
-    static_cast<float*>(a.out)[elem] = x;
-  } else if (a.out_kind == kBF16) {
-    static_cast<uint16_t*>(a.out)[elem] = f32_to_bf16_rne(x);
-  } else {
-    static_cast<uint16_t*>(a.out)[elem] = f32_to_f16_rne(x);
-  }
-}
-
-// Merge the waves of a workgroup (each left its max, sum and unnormalised
-// output in LDS) and write the result, or the partition's partial result.
-// The partition holds at least one token, so the merged max is finite.
-template <int GT, int D>
-__device__ __forceinline__ void finish_partition(const DecodeArgs& a, const float (&s_acc)[kWaves][GT][D],
-                                                 const float (&s_ml)[kWaves][GT][2], int seq, int h0, int part,
-                                                 int seq_parts, int tid) {
-  for (int idx = tid; idx < GT * D; idx += kThreads) {
-    const int g = idx / D;
-    const int d = idx - g * D;
-    float M = kNegInf;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_ml[w][g][0]);
-    float L = 0.f, O = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float f = fast_exp2(s_ml[w][g][0] - M);
-      L += s_ml[w][g][1] * f;
-      O += s_acc[w][g][d] * f;
-    }
-    O *= a.out_scale;
-    const int64_t sh = (int64_t)seq * a.num_heads + h0 + g;
-    if (seq_parts == 1) {
-      store_out(a, sh * D + d, O / L);
-    } else {
-      const int64_t pi = sh * a.num_parts + part;
-      a.ws_out[pi * D + d] = O;
-      if (d == 0) {
-        a.ws_ml[2 * pi] = M;
-        a.ws_ml[2 * pi + 1] = L;
-      }
-    }
-  }
-}
 
 template <int QK, int CK, int D, int GT>
 __global__ __launch_bounds__(kThreads) void decode_main(const DecodeArgs a) {
@@ -235,13 +181,11 @@ __global__ __launch_bounds__(kThreads) void decode_main(const DecodeArgs a) {
   const int seq = blockIdx.z;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  const int ctx = a.context_lens[seq];
-  if (ctx <= 0) {  // nothing to attend: zeros, written once by partition 0
-    if (part == 0)
-      for (int idx = tid; idx < GT * D; idx += kThreads)
-        store_out(a, ((int64_t)seq * a.num_heads + h0) * D + idx, 0.f);
+  const int ctx = context_len(a, seq);
+  if (ctx <= 0) {  // nothing to attend
+    write_zeros<GT, D>(a, seq, h0, part, tid);
     return;
   }
   const int seq_blocks = (ctx + 15) >> 4;
@@ -290,9 +234,13 @@ __global__ __launch_bounds__(kThreads) void decode_main(const DecodeArgs a) {
 
   // The tile address is wave-uniform (scalar registers); each lane adds its
   // 16-byte offset, so the loads take the scalar-base + vector-offset form.
-  auto load_tile = [&](int j, uint4 (&kr)[NL], uint4 (&vr)[NL]) {
-    const int phys = __builtin_amdgcn_readfirstlane(s_blocks[j]);
-    const int64_t off = (int64_t)phys * blk_stride;
+  struct Tile {
+    uint4 k[NL], v[NL];
+  };
+  auto load_tile = [&](int j, Tile& t) {
+    uint4(&kr)[NL] = t.k;
+    uint4(&vr)[NL] = t.v;
+    const int64_t off = pool_block(a, s_blocks, j) * blk_stride;
     const char* kt = kbase + off;
     const char* vt = vbase + off;
 #pragma unroll
@@ -301,7 +249,9 @@ __global__ __launch_bounds__(kThreads) void decode_main(const DecodeArgs a) {
     for (int i = 0; i < NL; ++i) vr[i] = load_stream(vt + lane_off + i * 1024);
   };
 
-  auto process = [&](int j, const uint4 (&kr)[NL], const uint4 (&vin)[NL]) {
+  auto process = [&](int j, const Tile& t) {
+    const uint4(&kr)[NL] = t.k;
+    const uint4(&vin)[NL] = t.v;
     float sc[GT][NL];
 #pragma unroll
     for (int i = 0; i < NL; ++i)
@@ -364,22 +314,7 @@ __global__ __launch_bounds__(kThreads) void decode_main(const DecodeArgs a) {
     }
   };
 
-  {
-    // Ring of kDepth register buffers: the tiles of the next kDepth-1 blocks
-    // of this wave are in flight while the current one is consumed.
-    uint4 kb[kDepth][NL], vb[kDepth][NL];
-#pragma unroll
-    for (int d = 0; d < kDepth - 1; ++d)
-      if (wave + d * kWaves < nblk) load_tile(wave + d * kWaves, kb[d], vb[d]);
-    for (int j = wave; j < nblk; j += kDepth * kWaves) {
-#pragma unroll
-      for (int d = 0; d < kDepth; ++d) {
-        const int jn = j + (d + kDepth - 1) * kWaves;
-        if (jn < nblk) load_tile(jn, kb[(d + kDepth - 1) % kDepth], vb[(d + kDepth - 1) % kDepth]);
-        if (j + d * kWaves < nblk) process(j + d * kWaves, kb[d], vb[d]);
-      }
-    }
-  }
+  stream_blocks<Tile>(wave, kWaves, nblk, load_tile, process);
 
   // Merge the RPL lane groups of this wave (they saw disjoint tokens).
 #pragma unroll
@@ -416,7 +351,7 @@ __global__ __launch_bounds__(kThreads) void decode_main(const DecodeArgs a) {
   }
   __syncthreads();
 
-  finish_partition<GT, D>(a, s_acc, s_ml, seq, h0, part, seq_parts, tid);
+  finish_partition<GT, D>(a, &s_acc[0][0][0], &s_ml[0][0][0], seq, h0, part, seq_parts, tid);
 }
 
 // Grouped-query decode for tiles of 4 or 8 query heads with 16-bit queries.
@@ -460,13 +395,11 @@ __global__ __launch_bounds__(kThreads) void decode_gqa(const DecodeArgs a) {
   const int seq = blockIdx.z;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  const int ctx = a.context_lens[seq];
+  const int ctx = context_len(a, seq);
   if (ctx <= 0) {
-    if (part == 0)
-      for (int idx = tid; idx < GT * D; idx += kThreads)
-        store_out(a, ((int64_t)seq * a.num_heads + h0) * D + idx, 0.f);
+    write_zeros<GT, D>(a, seq, h0, part, tid);
     return;
   }
   const int seq_blocks = (ctx + 15) >> 4;
@@ -519,9 +452,13 @@ __global__ __launch_bounds__(kThreads) void decode_gqa(const DecodeArgs a) {
   const int lane_off = r * (D * Geo::kBytes) + c * 16;
   const float qk_scale = a.qk_scale;
 
-  auto load_tile = [&](int j, uint4 (&kr)[NL], uint4 (&vr)[NL]) {
-    const int phys = __builtin_amdgcn_readfirstlane(s_blocks[j]);
-    const int64_t off = (int64_t)phys * blk_stride;
+  struct Tile {
+    uint4 k[NL], v[NL];
+  };
+  auto load_tile = [&](int j, Tile& t) {
+    uint4(&kr)[NL] = t.k;
+    uint4(&vr)[NL] = t.v;
+    const int64_t off = pool_block(a, s_blocks, j) * blk_stride;
     const char* kt = kbase + off;
     const char* vt = vbase + off;
 #pragma unroll
@@ -530,7 +467,12 @@ __global__ __launch_bounds__(kThreads) void decode_gqa(const DecodeArgs a) {
     for (int i = 0; i < NL; ++i) vr[i] = load_stream(vt + lane_off + i * 1024);
   };
 
-  auto process = [&](int j, const uint4 (&kr)[NL], const uint4 (&vin)[NL]) {
+  // kMasked: the block holds rows past the context (the last, partial block
+  // of a sequence); only that instantiation pays for the selects.
+  auto process = [&](auto masked, int j, const Tile& t) {
+    constexpr bool kMasked = decltype(masked)::value;
+    const uint4(&kr)[NL] = t.k;
+    const uint4(&vin)[NL] = t.v;
     float x[V0];  // x[g*NL + i] = partial q_g . k_(i*RPL + r) over this lane's slice
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
@@ -553,8 +495,8 @@ __global__ __launch_bounds__(kThreads) void decode_gqa(const DecodeArgs a) {
     uint4 vr[NL];
 #pragma unroll
     for (int i = 0; i < NL; ++i) vr[i] = vin[i];
-    const int tok0 = (blk0 + j) * 16;
-    if (tok0 + 16 > ctx) {  // last, partial block: drop rows past the context
+    if constexpr (kMasked) {  // last, partial block: drop rows past the context
+      const int tok0 = (blk0 + j) * 16;
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
         const bool ok = tok0 + i * RPL + r < ctx;
@@ -617,20 +559,14 @@ __global__ __launch_bounds__(kThreads) void decode_gqa(const DecodeArgs a) {
     }
   };
 
-  {
-    uint4 kb[kDepth][NL], vb[kDepth][NL];
-#pragma unroll
-    for (int d = 0; d < kDepth - 1; ++d)
-      if (wave + d * kWaves < nblk) load_tile(wave + d * kWaves, kb[d], vb[d]);
-    for (int j = wave; j < nblk; j += kDepth * kWaves) {
-#pragma unroll
-      for (int d = 0; d < kDepth; ++d) {
-        const int jn = j + (d + kDepth - 1) * kWaves;
-        if (jn < nblk) load_tile(jn, kb[(d + kDepth - 1) % kDepth], vb[(d + kDepth - 1) % kDepth]);
-        if (j + d * kWaves < nblk) process(j + d * kWaves, kb[d], vb[d]);
-      }
-    }
-  }
+  // Partition-relative index of the block holding rows past the context, if any.
+  const int masked_j = (ctx & 15) && blk0 + nblk == seq_blocks ? nblk - 1 : -1;
+  stream_blocks<Tile>(wave, kWaves, nblk, load_tile, [&](int j, const Tile& t) {
+    if (j != masked_j)
+      process(std::false_type{}, j, t);
+    else
+      process(std::true_type{}, j, t);
+  });
 
   // Merge the RPL rows of this wave: publish each (row, head) max and sum,
   // rescale the accumulators to the wave's max, then sum over the row lanes.
@@ -673,7 +609,7 @@ __global__ __launch_bounds__(kThreads) void decode_gqa(const DecodeArgs a) {
       for (int e = 0; e < E; ++e) s_acc[wave][g][c * E + e] = acc[g][e];
   }
   __syncthreads();
-  finish_partition<GT, D>(a, s_acc, s_ml, seq, h0, part, seq_parts, tid);
+  finish_partition<GT, D>(a, &s_acc[0][0][0], &s_ml[0][0][0], seq, h0, part, seq_parts, tid);
 }
 
 // Merge the partitions of every (sequence, head) whose context spans several.
@@ -682,7 +618,7 @@ __global__ __launch_bounds__(64) void decode_reduce(const DecodeArgs a) {
   const int h = blockIdx.x;
   const int seq = blockIdx.y;
   const int lane = threadIdx.x;
-  const int ctx = a.context_lens[seq];
+  const int ctx = context_len(a, seq);
   const int seq_parts = (((ctx + 15) >> 4) + a.partition_blocks - 1) / a.partition_blocks;
   if (seq_parts <= 1) return;  // written directly by decode_main
   const int64_t base = ((int64_t)seq * a.num_heads + h) * a.num_parts;
@@ -712,9 +648,6 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
     decode_gqa<QK, CK, D, GT><<<grid, dim3(kThreads), 0, stream>>>(a);
   else
     decode_main<QK, CK, D, GT><<<grid, dim3(kThreads), 0, stream>>>(a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.num_parts == 1) return e;
-  decode_reduce<D><<<dim3((unsigned)a.num_heads, (unsigned)a.num_seqs), dim3(64), 0, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -741,14 +674,26 @@ hipError_t launch_d(const DecodeArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, int q_kind, int cache_kind, hipStream_t stream) {
-  switch (q_kind * 4 + cache_kind) {
-    case kF32 * 4 + kF32: return launch_d<kF32, kF32>(a, stream);
-    case kF16 * 4 + kF16: return launch_d<kF16, kF16>(a, stream);
-    case kBF16 * 4 + kBF16: return launch_d<kBF16, kBF16>(a, stream);
-    case kF16 * 4 + kFP8: return launch_d<kF16, kFP8>(a, stream);
-    case kBF16 * 4 + kFP8: return launch_d<kBF16, kFP8>(a, stream);
+  hipError_t e;
+  if (a.use_mfma) {
+    e = launch_decode_mfma(a, q_kind, cache_kind, stream);
+  } else {
+    switch (q_kind * 4 + cache_kind) {
+      case kF32 * 4 + kF32: e = launch_d<kF32, kF32>(a, stream); break;
+      case kF16 * 4 + kF16: e = launch_d<kF16, kF16>(a, stream); break;
+      case kBF16 * 4 + kBF16: e = launch_d<kBF16, kBF16>(a, stream); break;
+      case kF16 * 4 + kFP8: e = launch_d<kF16, kFP8>(a, stream); break;
+      case kBF16 * 4 + kFP8: e = launch_d<kBF16, kFP8>(a, stream); break;
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if (e != hipSuccess || a.num_parts == 1) return e;
+  switch (a.head_size) {
+    case 64: decode_reduce<64><<<dim3((unsigned)a.num_heads, (unsigned)a.num_seqs), dim3(64), 0, stream>>>(a); break;
+    case 128: decode_reduce<128><<<dim3((unsigned)a.num_heads, (unsigned)a.num_seqs), dim3(64), 0, stream>>>(a); break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
 }
 
 }  // namespace pa

@@ -1,0 +1,123 @@
+// Pieces shared by the decode kernels: workgroup shape, streaming tile loads,
+// LDS ordering inside a wave, output rounding, and the per-workgroup epilogue
+// that merges the waves' running (max, sum, unnormalised output).
+#pragma once
+
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// Orders LDS traffic between lanes of one wave: the LDS executes one wave's
+// instructions in order, so only the compiler has to be kept from moving them.
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// K/V tiles are read once per step: nontemporal loads keep them from
+// displacing reusable lines in the caches.
+__device__ __forceinline__ uint4 load_stream(const char* p) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ void store_out(const DecodeArgs& a, int64_t elem, float x) {
+  if (a.out_kind == kF32) {
+    static_cast<float*>(a.out)[elem] = x;
+  } else if (a.out_kind == kBF16) {
+    static_cast<uint16_t*>(a.out)[elem] = f32_to_bf16_rne(x);
+  } else {
+    static_cast<uint16_t*>(a.out)[elem] = f32_to_f16_rne(x);
+  }
+}
+
+// Merge the waves of a workgroup (each left its max, sum and unnormalised
+// output in LDS: s_acc is [kWaves][GT][D], s_ml is [kWaves][GT][2]) and write
+// the result, or the partition's partial result. The partition holds at least
+// one token, so the merged max is finite.
+template <int GT, int D>
+__device__ __forceinline__ void finish_partition(const DecodeArgs& a, const float* s_acc, const float* s_ml, int seq,
+                                                 int h0, int part, int seq_parts, int tid) {
+  for (int idx = tid; idx < GT * D; idx += kThreads) {
+    const int g = idx / D;
+    const int d = idx - g * D;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_ml[(w * GT + g) * 2]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float f = fast_exp2(s_ml[(w * GT + g) * 2] - M);
+      L += s_ml[(w * GT + g) * 2 + 1] * f;
+      O += s_acc[(w * GT + g) * D + d] * f;
+    }
+    O *= a.out_scale;
+    const int64_t sh = (int64_t)seq * a.num_heads + h0 + g;
+    if (seq_parts == 1) {
+      store_out(a, sh * D + d, O / L);
+    } else {
+      const int64_t pi = sh * a.num_parts + part;
+      a.ws_out[pi * D + d] = O;
+      if (d == 0) {
+        a.ws_ml[2 * pi] = M;
+        a.ws_ml[2 * pi + 1] = L;
+      }
+    }
+  }
+}
+
+// Context length of a sequence, clamped to what its block-table row can hold,
+// so a length past the row never sends a kernel beyond the table.
+__device__ __forceinline__ int context_len(const DecodeArgs& a, int seq) {
+  return min(a.context_lens[seq], a.max_blocks * 16);
+}
+
+// Physical block of table entry j (wave-uniform); an id outside the pool is
+// clamped into it, so a corrupt table reads wrong data but no foreign memory.
+__device__ __forceinline__ int64_t pool_block(const DecodeArgs& a, const int* s_blocks, int j) {
+  const int phys = __builtin_amdgcn_readfirstlane(s_blocks[j]);
+  return (uint32_t)phys < (uint64_t)a.num_blocks ? phys : 0;
+}
+
+// Streams blocks j = first, first + step, ... < n through a two-stage register
+// ring: block j + step's loads are issued before block j is processed. The
+// steady-state loop issues them unconditionally, so the compiler's wait for
+// block j's registers counts the newer loads and leaves them in flight while
+// j is processed; a conditional prefetch would join two paths with different
+// numbers of outstanding loads and force a wait for all of them.
+template <class Buf, class Load, class Proc>
+__device__ __forceinline__ void stream_blocks(int first, int step, int n, Load&& load, Proc&& proc) {
+  if (first >= n) return;
+  Buf b0, b1;
+  int j = first;
+  load(j, b0);
+  for (; j + 2 * step < n; j += 2 * step) {
+    load(j + step, b1);
+    proc(j, b0);
+    load(j + 2 * step, b0);
+    proc(j + step, b1);
+  }
+  if (j + step < n) {
+    load(j + step, b1);
+    proc(j, b0);
+    proc(j + step, b1);
+  } else {
+    proc(j, b0);
+  }
+}
+
+// Zeros for a sequence with nothing to attend, written once (by partition 0).
+template <int GT, int D>
+__device__ __forceinline__ void write_zeros(const DecodeArgs& a, int seq, int h0, int part, int tid) {
+  if (part == 0)
+    for (int idx = tid; idx < GT * D; idx += kThreads) store_out(a, ((int64_t)seq * a.num_heads + h0) * D + idx, 0.f);
+}
+
+}  // namespace pa

@@ -1,0 +1,377 @@
+// Grouped-query paged decode on the gfx950 matrix cores, for 16-bit queries.
+//
+// Same result as the vector-ALU kernels in pa_decode.hip: softmax(q·Kᵀ·scale)·V
+// per query head over the sequence's cached tokens, reached through its block
+// table ("vLLM 前世今生" §3.2; "vLLM" note, sections "PagedAttention" and
+// "内核优化", where a group of query heads shares one KV head).
+//
+// With GT query heads per KV head, one (block, KV head) tile of 16 tokens is a
+// small dense contraction, not a matrix-vector product: S = K·Qᵀ is
+// [16 tokens × D]·[D × GT heads] and O += P·V is [GT × 16]·[16 × D]. On the
+// vector ALU these products cost about 600 instructions per tile at GT = 8,
+// which leaves the kernel ALU-bound below the HBM roofline; here they are
+// issued as MFMA instructions (16×16×32 for S, 16×16×16 for O), and the
+// vector ALU only runs the online softmax.
+//
+//  * One workgroup of 4 waves per (sequence, KV head, head tile of GT <= 16,
+//    partition), wave w taking blocks w, w+4, ... of the partition, exactly as
+//    the vector kernels do, with the block-table slice staged in LDS and the
+//    next block's K/V loads in flight while the current one is used.
+//  * K is loaded straight from HBM in the MFMA A-operand layout: lane l reads
+//    16 bytes of token l % 16 (64 contiguous bytes per token per instruction),
+//    so S needs no data movement at all. The head dimension may be taken in
+//    any order as long as q is read in the same order (a dot product does not
+//    care), which lets FP8 rows be read 16 bytes at a time.
+//  * S comes out with lane l holding head l % 16 for tokens 4·(l/16) + i,
+//    which is exactly the A-operand layout of P in O += P·V: the softmax runs
+//    in place, per lane, with no shuffle of P.
+//  * V must be read token-major per lane, so each wave stages its V tile in
+//    LDS (rows padded by 16 bytes against bank conflicts; FP8 widened to the
+//    16-bit type on the way) and reads the B operand with 2-byte loads.
+//  * P is rounded to the 16-bit type as hi + lo (two MFMAs per D-slice), so the
+//    weights keep about 16 significant bits and the output stays within float32
+//    accumulation error of the exact weights; V, K and q are exact in the
+//    16-bit type (FP8 codes widen exactly).
+//  * The running max is moved lazily: only when a tile's max exceeds it by more
+//    than kSlack (log2 units) is it raised and the accumulators rescaled; all
+//    weights stay below 2^kSlack, which float32 sums hold easily.
+// Rows past the context get a -inf logit by selection and a zero V row, so
+// stale or NaN data there never reaches the output.
+#include <type_traits>
+
+#include "pa_decode_common.h"
+
+namespace pa {
+namespace {
+
+constexpr float kSlack = 8.0f;    // lazy-max slack, log2 units
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// C += A·B over 32 k (8 elements of A and of B per lane, 4 words each).
+template <int QK>
+__device__ __forceinline__ f32x4_t mma_k32(const uint32_t* a, const uint32_t* b, f32x4_t c) {
+  const u32x4_t av = {a[0], a[1], a[2], a[3]};
+  const u32x4_t bv = {b[0], b[1], b[2], b[3]};
+  if constexpr (QK == kBF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, bv),
+                                                   c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, av), __builtin_bit_cast(f16x8_t, bv), c,
+                                                  0, 0, 0);
+}
+
+// C += A·B over 16 k (4 elements of A and of B per lane, 2 words each).
+template <int QK>
+__device__ __forceinline__ f32x4_t mma_k16(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, f32x4_t c) {
+  const u32x2_t av = {a0, a1};
+  const u32x2_t bv = {b0, b1};
+  if constexpr (QK == kBF16)
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, av), __builtin_bit_cast(i16x4_t, bv),
+                                                     c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, av), __builtin_bit_cast(f16x4_t, bv), c,
+                                                 0, 0, 0);
+}
+
+// Two float32 -> two 16-bit values of the query's type (nearest-even), packed.
+template <int QK>
+__device__ __forceinline__ uint32_t pack2(float x, float y) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  if constexpr (QK == kBF16) {
+    typedef __bf16 h2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){x, y}, h2));
+  } else {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){x, y}, h2));
+  }
+}
+
+template <int QK> __device__ __forceinline__ float lo16_to_f32(uint32_t w) {
+  return QK == kBF16 ? bf16_lo(w) : f16_lo(w);
+}
+template <int QK> __device__ __forceinline__ float hi16_to_f32(uint32_t w) {
+  return QK == kBF16 ? bf16_hi(w) : f16_hi(w);
+}
+
+// Four FP8 codes -> four values of the query's 16-bit type (exact), as two words.
+template <int QK>
+__device__ __forceinline__ void fp8x4_to_16(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  if constexpr (QK == kBF16) {
+    lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, false));
+    hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, true));
+  } else {
+    lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w, 1.0f, false));
+    hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w, 1.0f, true));
+  }
+}
+
+// Geometry of one (block, KV head) tile for the MFMA kernel.
+template <int CK, int D> struct MGeo {
+  static constexpr int kBytes = KindBytes<CK>::value;
+  static constexpr int kRowBytes = D * kBytes;
+  static constexpr int kTileBytes = 16 * kRowBytes;
+  static constexpr int NKB = D / 32;                      // 32-wide k blocks of S
+  static constexpr int NKL = (CK == kFP8) ? D / 64 : D / 32;  // K loads per lane (16 bytes each)
+  static constexpr int NVL = kTileBytes / 1024;           // V loads per lane (16 bytes each)
+  static constexpr int NDB = D / 16;                      // 16-wide column blocks of O
+  static constexpr int kVStride = D + 8;                  // LDS row stride of the staged V tile (16-bit elements)
+  static_assert(NVL >= 1, "tile smaller than one wave-load");
+};
+
+// First element (along D) of the 8 q/K elements lane group g supplies to k block b.
+template <int CK> __device__ __forceinline__ constexpr int k_col(int b, int g) {
+  return CK == kFP8 ? 64 * (b >> 1) + 16 * g + 8 * (b & 1) : 32 * b + 8 * g;
+}
+
+template <int QK, int CK, int D, int GT>
+__global__ __launch_bounds__(kThreads) void decode_mfma(const DecodeArgs a) {
+  using G = MGeo<CK, D>;
+  constexpr int NKB = G::NKB, NKL = G::NKL, NVL = G::NVL, NDB = G::NDB, VS = G::kVStride;
+  static_assert(QK == kF16 || QK == kBF16, "16-bit queries");
+  static_assert(GT == 4 || GT == 8 || GT == 16, "head tile of 4, 8 or 16");
+
+  __shared__ int s_blocks[kMaxPartitionBlocks];
+  __shared__ __align__(16) uint16_t s_v[kWaves][16 * VS];
+  __shared__ float s_acc[kWaves * GT * D];
+  __shared__ float s_ml[kWaves * GT * 2];
+
+  const int n_sub = a.group / GT;
+  const int kvh = blockIdx.x / n_sub;
+  const int h0 = kvh * a.group + (blockIdx.x - kvh * n_sub) * GT;
+  const int part = blockIdx.y;
+  const int seq = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15;  // token of K rows / head of S columns and P rows / column of O
+  const int g = lane >> 4;  // k group of the operands / row group of the results
+
+  const int ctx = context_len(a, seq);
+  if (ctx <= 0) {
+    write_zeros<GT, D>(a, seq, h0, part, tid);
+    return;
+  }
+  const int seq_blocks = (ctx + 15) >> 4;
+  const int blk0 = part * a.partition_blocks;
+  if (blk0 >= seq_blocks) return;
+  const int nblk = min(a.partition_blocks, seq_blocks - blk0);
+  const int seq_parts = (seq_blocks + a.partition_blocks - 1) / a.partition_blocks;
+
+  const int32_t* bt = a.block_tables + (int64_t)seq * a.max_blocks + blk0;
+  for (int j = tid; j < nblk; j += kThreads) s_blocks[j] = bt[j];
+
+  // q as the B operand of S = K·Qᵀ: lane (n, g) holds head h0 + n, the 8
+  // elements of k block b that group g supplies; heads past the tile are zero.
+  uint32_t qf[NKB][4];
+  {
+    const char* qp = static_cast<const char*>(a.q) + ((int64_t)seq * a.num_heads + h0 + n) * D * 2;
+#pragma unroll
+    for (int b = 0; b < NKB; ++b) {
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (n < GT) v = *reinterpret_cast<const uint4*>(qp + k_col<CK>(b, g) * 2);
+      qf[b][0] = v.x;
+      qf[b][1] = v.y;
+      qf[b][2] = v.z;
+      qf[b][3] = v.w;
+    }
+  }
+  __syncthreads();
+
+  f32x4_t acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  float mref = kNegInf;  // running reference max of head n (log2 units), equal on lanes n, n+16, n+32, n+48
+  float lsum = 0.f;      // this lane's share of the running sum of head n
+
+  const int64_t blk_stride = (int64_t)a.num_kv_heads * G::kTileBytes;
+  const char* kbase = static_cast<const char*>(a.k_cache) + (int64_t)kvh * G::kTileBytes;
+  const char* vbase = static_cast<const char*>(a.v_cache) + (int64_t)kvh * G::kTileBytes;
+  const int k_off = n * G::kRowBytes + g * 16;  // + 64 * load
+  const int v_off = lane * 16;                  // + 1024 * load
+  const float qk_scale = a.qk_scale;
+  uint16_t* sv = s_v[wave];
+
+  struct Tile {
+    uint4 k[NKL], v[NVL];
+  };
+  auto load_tile = [&](int j, Tile& t) {
+    uint4(&kr)[NKL] = t.k;
+    uint4(&vr)[NVL] = t.v;
+    const int64_t off = pool_block(a, s_blocks, j) * blk_stride;
+    const char* kt = kbase + off;
+    const char* vt = vbase + off;
+#pragma unroll
+    for (int c = 0; c < NKL; ++c) kr[c] = load_stream(kt + k_off + c * 64);
+#pragma unroll
+    for (int c = 0; c < NVL; ++c) vr[c] = load_stream(vt + v_off + c * 1024);
+  };
+
+  auto process = [&](auto masked, int j, const Tile& t) {
+    constexpr bool kMasked = decltype(masked)::value;
+    const uint4(&kr)[NKL] = t.k;
+    const uint4(&vr)[NVL] = t.v;
+    const int valid = kMasked ? ctx - (blk0 + j) * 16 : 16;  // token rows of this block inside the context
+
+    // Stage V (row-major, 16-bit) for the transposed operand reads.
+    wave_lds_fence();  // the previous block's reads of sv are issued before it is overwritten
+#pragma unroll
+    for (int c = 0; c < NVL; ++c) {
+      const int byte = c * 1024 + lane * 16;
+      const int row = byte / G::kRowBytes;
+      const int col = (byte % G::kRowBytes) / G::kBytes;
+      const bool keep = !kMasked || row < valid;
+      uint4 v = vr[c];
+      if constexpr (CK == kFP8) {
+        uint4 w0, w1;
+        fp8x4_to_16<QK>(v.x, w0.x, w0.y);
+        fp8x4_to_16<QK>(v.y, w0.z, w0.w);
+        fp8x4_to_16<QK>(v.z, w1.x, w1.y);
+        fp8x4_to_16<QK>(v.w, w1.z, w1.w);
+        if (!keep) w0 = w1 = make_uint4(0u, 0u, 0u, 0u);
+        *reinterpret_cast<uint4*>(sv + row * VS + col) = w0;
+        *reinterpret_cast<uint4*>(sv + row * VS + col + 8) = w1;
+      } else {
+        if (!keep) v = make_uint4(0u, 0u, 0u, 0u);
+        *reinterpret_cast<uint4*>(sv + row * VS + col) = v;
+      }
+    }
+
+    // S = K·Qᵀ: lane (n, g) ends with the logits of head n for tokens 4g + i.
+    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (CK == kFP8) {
+#pragma unroll
+      for (int c = 0; c < NKL; ++c) {
+        uint32_t w[8];
+        fp8x4_to_16<QK>(kr[c].x, w[0], w[1]);
+        fp8x4_to_16<QK>(kr[c].y, w[2], w[3]);
+        fp8x4_to_16<QK>(kr[c].z, w[4], w[5]);
+        fp8x4_to_16<QK>(kr[c].w, w[6], w[7]);
+        s = mma_k32<QK>(w, qf[2 * c], s);
+        s = mma_k32<QK>(w + 4, qf[2 * c + 1], s);
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < NKL; ++c) {
+        const uint32_t w[4] = {kr[c].x, kr[c].y, kr[c].z, kr[c].w};
+        s = mma_k32<QK>(w, qf[c], s);
+      }
+    }
+
+    float x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[i] = s[i] * qk_scale;
+      if (n >= GT || (kMasked && 4 * g + i >= valid)) x[i] = kNegInf;
+    }
+    const float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    if (__builtin_amdgcn_ballot_w64(bm > mref + kSlack) != 0) {  // raise the reference max (wave-uniform)
+      float bmx = fmaxf(bm, __shfl_xor(bm, 16, 64));
+      bmx = fmaxf(bmx, __shfl_xor(bmx, 32, 64));
+      const float mn = fmaxf(mref, bmx);
+      const float alpha = fast_exp2(mref - ((mn == kNegInf) ? 0.f : mn));
+      lsum *= alpha;
+      mref = mn;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float al = __shfl(alpha, 4 * g + i, 64);  // the factor of head 4g + i (rows of acc)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) acc[db][i] *= al;
+      }
+    }
+    const float ms = (mref == kNegInf) ? 0.f : mref;
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = fast_exp2(x[i] - ms);
+      lsum += p[i];
+    }
+    // P as hi + lo in the 16-bit type (the A operand: head n, tokens 4g .. 4g+3).
+    const uint32_t h01 = pack2<QK>(p[0], p[1]);
+    const uint32_t h23 = pack2<QK>(p[2], p[3]);
+    const uint32_t l01 = pack2<QK>(p[0] - lo16_to_f32<QK>(h01), p[1] - hi16_to_f32<QK>(h01));
+    const uint32_t l23 = pack2<QK>(p[2] - lo16_to_f32<QK>(h23), p[3] - hi16_to_f32<QK>(h23));
+
+    wave_lds_fence();  // the staged V tile is written
+    const uint16_t* vrow = sv + 4 * g * VS + n;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const uint32_t b0 = (uint32_t)vrow[db * 16] | ((uint32_t)vrow[VS + db * 16] << 16);
+      const uint32_t b1 = (uint32_t)vrow[2 * VS + db * 16] | ((uint32_t)vrow[3 * VS + db * 16] << 16);
+      acc[db] = mma_k16<QK>(h01, h23, b0, b1, acc[db]);
+      acc[db] = mma_k16<QK>(l01, l23, b0, b1, acc[db]);
+    }
+  };
+
+  // Partition-relative index of the block holding rows past the context, if any.
+  const int masked_j = (ctx & 15) && blk0 + nblk == seq_blocks ? nblk - 1 : -1;
+  stream_blocks<Tile>(wave, kWaves, nblk, load_tile, [&](int j, const Tile& t) {
+    if (j != masked_j)
+      process(std::false_type{}, j, t);
+    else
+      process(std::true_type{}, j, t);
+  });
+
+  // This wave's sum of head n over its four row groups; the max is already shared.
+  lsum += __shfl_xor(lsum, 16, 64);
+  lsum += __shfl_xor(lsum, 32, 64);
+  if (g == 0 && n < GT) {
+    s_ml[(wave * GT + n) * 2] = mref;
+    s_ml[(wave * GT + n) * 2 + 1] = lsum;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (4 * g + i < GT) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) s_acc[(wave * GT + 4 * g + i) * D + db * 16 + n] = acc[db][i];
+    }
+  }
+  __syncthreads();
+  finish_partition<GT, D>(a, s_acc, s_ml, seq, h0, part, seq_parts, tid);
+}
+
+template <int QK, int CK, int D, int GT>
+hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
+  const dim3 grid((unsigned)(a.num_kv_heads * (a.group / GT)), (unsigned)a.num_parts, (unsigned)a.num_seqs);
+  decode_mfma<QK, CK, D, GT><<<grid, dim3(kThreads), 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+template <int QK, int CK, int D>
+hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
+  switch (a.group_tile) {
+    case 4: return launch_t<QK, CK, D, 4>(a, stream);
+    case 8: return launch_t<QK, CK, D, 8>(a, stream);
+    case 16: return launch_t<QK, CK, D, 16>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int QK, int CK>
+hipError_t launch_d(const DecodeArgs& a, hipStream_t stream) {
+  switch (a.head_size) {
+    case 64: return launch_g<QK, CK, 64>(a, stream);
+    case 128: return launch_g<QK, CK, 128>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode_mfma(const DecodeArgs& a, int q_kind, int cache_kind, hipStream_t stream) {
+  switch (q_kind * 4 + cache_kind) {
+    case kF16 * 4 + kF16: return launch_d<kF16, kF16>(a, stream);
+    case kBF16 * 4 + kBF16: return launch_d<kBF16, kBF16>(a, stream);
+    case kF16 * 4 + kFP8: return launch_d<kF16, kFP8>(a, stream);
+    case kBF16 * 4 + kFP8: return launch_d<kBF16, kFP8>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace pa

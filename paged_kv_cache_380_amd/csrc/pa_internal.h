@@ -14,6 +14,7 @@ struct ReshapeArgs {
   void* v_cache;
   const void* slots;
   int64_t num_tokens;
+  int64_t num_blocks;     // pool size; slots at or past num_blocks * 16 are skipped
   int num_kv_heads;
   int head_size;
   int slot_is_int64;
@@ -41,19 +42,31 @@ struct DecodeArgs {
   int head_size;
   int group;              // num_heads / num_kv_heads
   int group_tile;         // query heads handled by one workgroup (divides group)
+  int64_t num_blocks;     // pool size (block ids outside [0, num_blocks) are clamped)
   int max_blocks;         // block table row length
   int partition_blocks;   // blocks per partition
   int num_parts;          // ceil(max_blocks / partition_blocks)
   int out_kind;           // Kind of out: F32 or the query kind
+  int use_mfma;           // 1: matrix-core kernel (16-bit queries, group_tile 4, 8 or 16)
 };
 
+// Queues the decode kernel(s) chosen by a.use_mfma, then the partition merge if needed.
 hipError_t launch_decode(const DecodeArgs& a, int q_kind, int cache_kind, hipStream_t stream);
+// The matrix-core decode kernel alone (pa_decode_mfma.hip).
+hipError_t launch_decode_mfma(const DecodeArgs& a, int q_kind, int cache_kind, hipStream_t stream);
 
 // Largest query-head tile (8, 4, 2 or 1) dividing the group size.
 inline int group_tile_for(int group) {
   for (int t = 8; t > 1; t /= 2)
     if (group % t == 0) return t;
   return 1;
+}
+
+// Query-head tile of the matrix-core kernel (16, 8 or 4 dividing the group), or 0 if none does.
+inline int mfma_group_tile(int group) {
+  for (int t = 16; t >= 4; t /= 2)
+    if (group % t == 0) return t;
+  return 0;
 }
 
 constexpr int kMaxPartitionBlocks = 512;

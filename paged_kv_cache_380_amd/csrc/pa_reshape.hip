@@ -58,7 +58,7 @@ __global__ __launch_bounds__(kThreads) void reshape_kernel(ReshapeArgs a) {
   const int rem = (int)(idx - t * chunks_per_tok);
   const int64_t slot = a.slot_is_int64 ? static_cast<const int64_t*>(a.slots)[t]
                                        : (int64_t) static_cast<const int32_t*>(a.slots)[t];
-  if (slot < 0) return;
+  if (slot < 0 || slot >= a.num_blocks * 16) return;  // padding, or outside the pool
   const int head = rem / chunks_per_row;
   const int chunk = rem - head * chunks_per_row;
   const int64_t blk = slot >> 4;  // block_size is 16

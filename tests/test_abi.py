@@ -121,7 +121,7 @@ def test_workspace_bytes_formula(lib):
 def test_partition_choice(lib):
     pb = binding.decode_partition_blocks
     assert pb(32, 32, 32, 128, 128) == 128        # 1024 (seq, head) tiles: no split
-    assert pb(8, 64, 8, 128, 2048) == 128         # 64 tiles: 16 partitions of 2048 tokens
+    assert pb(8, 64, 8, 128, 2048) == 256         # 64 tiles: 8 partitions of 4096 tokens
     assert pb(4, 8, 8, 64, 16) == 4               # tiny: finest split
     for args in [(64, 32, 8, 128, 256), (256, 32, 8, 128, 192), (1, 1, 1, 64, 1)]:
         p = pb(*args)
