@@ -31,6 +31,14 @@ HIPCC_FLAGS = [
 ]
 
 
+# Per-source additions. The matrix-core decode keeps its MFMA accumulators in
+# ordinary VGPRs: with the default AGPR form the compiler copied all 32
+# accumulators out of and back into AGPRs on every block.
+FILE_FLAGS = {
+    "pa_decode_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def hipcc() -> str:
     path = os.environ.get("HIPCC") or shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(path):
@@ -57,7 +65,8 @@ def build(verbose: bool = False, extra_flags=()) -> str:
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     objs = [os.path.join(BUILD, os.path.basename(s)[:-4] + ".o") for s in srcs]
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        futs = [ex.submit(_run, [cc, *HIPCC_FLAGS, *extra_flags, "-c", s, "-o", o], verbose)
+        futs = [ex.submit(_run, [cc, *HIPCC_FLAGS, *FILE_FLAGS.get(os.path.basename(s), []), *extra_flags,
+                                 "-c", s, "-o", o], verbose)
                 for s, o in zip(srcs, objs)]
         for f in futs:
             f.result()

@@ -32,6 +32,8 @@
 namespace pa {
 namespace {
 
+constexpr int kRing = 2;  // register ring depth: blocks per wave in flight, plus the one in use
+
 
 template <int QK, int CK, int D> struct QFrag {
   static constexpr int kElems = TileGeo<CK, D>::E;                     // q elements per lane
@@ -314,7 +316,7 @@ __global__ __launch_bounds__(kThreads) void decode_main(const DecodeArgs a) {
     }
   };
 
-  stream_blocks<Tile>(wave, kWaves, nblk, load_tile, process);
+  stream_blocks<kRing, Tile>(wave, kWaves, nblk, load_tile, process);
 
   // Merge the RPL lane groups of this wave (they saw disjoint tokens).
 #pragma unroll
@@ -561,7 +563,7 @@ __global__ __launch_bounds__(kThreads) void decode_gqa(const DecodeArgs a) {
 
   // Partition-relative index of the block holding rows past the context, if any.
   const int masked_j = (ctx & 15) && blk0 + nblk == seq_blocks ? nblk - 1 : -1;
-  stream_blocks<Tile>(wave, kWaves, nblk, load_tile, [&](int j, const Tile& t) {
+  stream_blocks<kRing, Tile>(wave, kWaves, nblk, load_tile, [&](int j, const Tile& t) {
     if (j != masked_j)
       process(std::false_type{}, j, t);
     else

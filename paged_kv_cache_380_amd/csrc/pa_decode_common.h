@@ -86,30 +86,63 @@ __device__ __forceinline__ int64_t pool_block(const DecodeArgs& a, const int* s_
   return (uint32_t)phys < (uint64_t)a.num_blocks ? phys : 0;
 }
 
-// Streams blocks j = first, first + step, ... < n through a two-stage register
-// ring: block j + step's loads are issued before block j is processed. The
-// steady-state loop issues them unconditionally, so the compiler's wait for
-// block j's registers counts the newer loads and leaves them in flight while
-// j is processed; a conditional prefetch would join two paths with different
-// numbers of outstanding loads and force a wait for all of them.
-template <class Buf, class Load, class Proc>
+// Streams blocks j = first, first + step, ... < n through a ring of N register
+// buffers: the loads of the next N-1 blocks are in flight while a block is
+// processed. The steady-state loop issues its loads unconditionally, so the
+// compiler's wait for a block's registers counts the newer loads and leaves
+// them in flight; a conditional prefetch would join two paths with different
+// numbers of outstanding loads and force a wait for all of them. Scheduling
+// barriers keep the compiler from hoisting work of a block just requested
+// above the point where it is requested (which would again wait for it) or
+// from sinking loads below the processing.
+template <int N, class Buf, class Load, class Proc>
 __device__ __forceinline__ void stream_blocks(int first, int step, int n, Load&& load, Proc&& proc) {
+  static_assert(N >= 2, "ring of at least two buffers");
   if (first >= n) return;
-  Buf b0, b1;
-  int j = first;
-  load(j, b0);
-  for (; j + 2 * step < n; j += 2 * step) {
-    load(j + step, b1);
-    proc(j, b0);
-    load(j + 2 * step, b0);
-    proc(j + step, b1);
+  if constexpr (N == 2) {  // written out: fewer live registers than the general tail
+    Buf b0, b1;
+    int j = first;
+    load(j, b0);
+    for (; j + 2 * step < n; j += 2 * step) {
+      load(j + step, b1);
+      __builtin_amdgcn_sched_barrier(0);
+      proc(j, b0);
+      __builtin_amdgcn_sched_barrier(0);
+      load(j + 2 * step, b0);
+      __builtin_amdgcn_sched_barrier(0);
+      proc(j + step, b1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (j + step < n) {
+      load(j + step, b1);
+      __builtin_amdgcn_sched_barrier(0);
+      proc(j, b0);
+      __builtin_amdgcn_sched_barrier(0);
+      proc(j + step, b1);
+    } else {
+      proc(j, b0);
+    }
+    return;
   }
-  if (j + step < n) {
-    load(j + step, b1);
-    proc(j, b0);
-    proc(j + step, b1);
-  } else {
-    proc(j, b0);
+  Buf b[N];
+#pragma unroll
+  for (int d = 0; d < N - 1; ++d)
+    if (first + d * step < n) load(first + d * step, b[d]);
+  int j = first;
+  for (; j + (2 * N - 2) * step < n; j += N * step) {
+#pragma unroll
+    for (int d = 0; d < N; ++d) {
+      load(j + (d + N - 1) * step, b[(d + N - 1) % N]);
+      __builtin_amdgcn_sched_barrier(0);
+      proc(j + d * step, b[d]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  // Tail: blocks j + d*step < n for d < 2N-2; those with d < N-1 are loaded.
+#pragma unroll
+  for (int d = 0; d < 2 * N - 2; ++d) {
+    if (d + N - 1 < 2 * N - 2 && j + (d + N - 1) * step < n) load(j + (d + N - 1) * step, b[(d + N - 1) % N]);
+    if (j + d * step < n) proc(j + d * step, b[d % N]);
   }
 }
 

@@ -45,6 +45,7 @@ namespace pa {
 namespace {
 
 constexpr float kSlack = 8.0f;    // lazy-max slack, log2 units
+constexpr int kRing = 2;          // register ring depth: blocks per wave in flight, plus the one in use
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
@@ -309,14 +310,19 @@ __global__ __launch_bounds__(kThreads) void decode_mfma(const DecodeArgs a) {
     }
   };
 
-  // Partition-relative index of the block holding rows past the context, if any.
-  const int masked_j = (ctx & 15) && blk0 + nblk == seq_blocks ? nblk - 1 : -1;
-  stream_blocks<Tile>(wave, kWaves, nblk, load_tile, [&](int j, const Tile& t) {
-    if (j != masked_j)
-      process(std::false_type{}, j, t);
-    else
-      process(std::true_type{}, j, t);
-  });
+  // The block holding rows past the context (the last of the sequence, when
+  // its length is not a multiple of 16) runs after the steady stream, by the
+  // wave that owns it, so the stream's loop body holds one unmasked block
+  // per ring slot and the accumulators stay in place across iterations.
+  const bool tail_masked = (ctx & 15) && blk0 + nblk == seq_blocks;
+  const int n_full = nblk - (tail_masked ? 1 : 0);
+  stream_blocks<kRing, Tile>(wave, kWaves, n_full, load_tile,
+                      [&](int j, const Tile& t) { process(std::false_type{}, j, t); });
+  if (tail_masked && n_full % kWaves == wave) {
+    Tile t;
+    load_tile(n_full, t);
+    process(std::true_type{}, n_full, t);
+  }
 
   // This wave's sum of head n over its four row groups; the max is already shared.
   lsum += __shfl_xor(lsum, 16, 64);
