@@ -72,7 +72,9 @@ typedef enum pa_status {
   PA_ERR_SHAPE = 3,        /* a size is negative, zero where it must not be, or inconsistent */
   PA_ERR_UNSUPPORTED = 4,  /* block_size != 16, head_size not 64 or 128, too many query heads per KV head */
   PA_ERR_WORKSPACE = 5,    /* workspace missing, too small or misaligned */
-  PA_ERR_LAUNCH = 6        /* the HIP runtime rejected a kernel launch */
+  PA_ERR_LAUNCH = 6,       /* the HIP runtime rejected a kernel launch */
+  PA_ERR_CAPACITY = 7,     /* block manager: the pool or a sequence's table row is full */
+  PA_ERR_STATE = 8         /* block manager: unknown, duplicate or repeated sequence id */
 } pa_status;
 
 /*
@@ -175,6 +177,74 @@ size_t pa_decode_workspace_bytes(int num_seqs, int num_heads, int num_kv_heads, 
 /* Partition length (in blocks) pa_decode would choose for these shapes. */
 int pa_decode_partition_blocks(int num_seqs, int num_heads, int num_kv_heads, int head_size,
                                int max_blocks_per_seq, int block_size);
+
+/*
+ * pa_copy_blocks -- copy whole physical blocks, the device half of
+ * copy-on-write ("vLLM 前世今生" §3.2: a block shared by several sequences is
+ * copied before one of them writes into it).
+ *
+ * For i < num_pairs: block dst_blocks[i] of k_cache becomes a copy of block
+ * src_blocks[i] (all KV heads, all 16 rows), and the same in v_cache.
+ *
+ *   k_cache, v_cache   device, [num_blocks, num_kv_heads, block_size, head_size], cache_dtype
+ *   src_blocks, dst_blocks  device, int32 [num_pairs]; pairs as emitted by
+ *                      pa_bm_append_slots
+ *   num_pairs          0 .. 65535 (0 queues nothing)
+ *   block_size         must be 16; head_size 64 or 128
+ *
+ * Destinations must be distinct and no block may be both a source and a
+ * destination in one call (the copies run concurrently). A pair with an id
+ * outside [0, num_blocks), or with src == dst, copies nothing. Asynchronous on
+ * `stream`; must be queued before the reshape that writes into the copies.
+ */
+int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_blocks, const int32_t* dst_blocks, int num_pairs,
+                   int64_t num_blocks, int num_kv_heads, int head_size, int block_size, pa_dtype cache_dtype,
+                   void* stream);
+
+/*
+ * Block manager -- host-side bookkeeping of the block pool ("vLLM 前世今生"
+ * §3.2 and §3.3; "vLLM" note, section "PagedAttention"): blocks are taken from
+ * a free list as sequences grow and returned when they finish (both O(1));
+ * a forked sequence shares its parent's blocks (reference counts); appending
+ * to a sequence whose last, partly filled block is shared first moves the
+ * sequence to a private copy (copy-on-write), reported as a (source,
+ * destination) pair for pa_copy_blocks.
+ *
+ * All functions run on the host, touch no device memory, and are not
+ * thread-safe for one manager (callers serialise). Status codes as above;
+ * a failing call changes nothing.
+ */
+typedef struct pa_block_manager pa_block_manager;
+
+/* New manager of blocks 0 .. num_blocks-1 (all free); NULL on bad arguments.
+ * block_size must be 16; a sequence may hold at most max_blocks_per_seq blocks. */
+pa_block_manager* pa_bm_create(int64_t num_blocks, int block_size, int max_blocks_per_seq);
+void pa_bm_destroy(pa_block_manager* bm);
+/* Blocks on the free list (-1 for NULL). */
+int64_t pa_bm_num_free_blocks(const pa_block_manager* bm);
+/* Reference count of a block (0 = free), or -1 for an id outside the pool. */
+int pa_bm_block_refcount(const pa_block_manager* bm, int32_t block);
+/* Registers an empty sequence (PA_ERR_STATE if the id exists). */
+int pa_bm_add_sequence(pa_block_manager* bm, int64_t seq_id);
+/* New sequence `child` sharing all of `parent`'s blocks and its length. */
+int pa_bm_fork(pa_block_manager* bm, int64_t parent, int64_t child);
+/* Drops a sequence; blocks no other sequence holds return to the free list. */
+int pa_bm_free_sequence(pa_block_manager* bm, int64_t seq_id);
+/*
+ * Appends one token to each of n distinct sequences, in order. slots_out[i]
+ * (host, int64 [n]) receives the slot (block * 16 + row) where sequence i's
+ * new token is to be written (pa_reshape_and_cache). A sequence at a block
+ * boundary takes a fresh block; one whose partly filled last block is shared
+ * takes a fresh block too, and the pair (shared, fresh) is appended to
+ * cow_src / cow_dst (host, int32, room for n each), their count to *num_cow.
+ * PA_ERR_CAPACITY if the free blocks do not suffice or a row would overflow.
+ */
+int pa_bm_append_slots(pa_block_manager* bm, const int64_t* seq_ids, int n, int64_t* slots_out, int32_t* cow_src,
+                       int32_t* cow_dst, int* num_cow);
+/* Dense tables for n sequences: tables_out (host, int32 [n, max_blocks]) gets
+ * each sequence's blocks padded with -1, lens_out (host, int32 [n]) its length. */
+int pa_bm_block_tables(const pa_block_manager* bm, const int64_t* seq_ids, int n, int32_t* tables_out, int max_blocks,
+                       int32_t* lens_out);
 
 /* Message for the last non-zero status returned on this thread ("" if none). */
 const char* pa_last_error(void);

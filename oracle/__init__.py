@@ -32,6 +32,7 @@ cast). No function in this package is "parity unpinned".
 from .e4m3 import e4m3_code_values, e4m3_decode, e4m3_encode
 from .paged_attention import (
     DTYPES,
+    copy_blocks,
     decode_attention,
     quantize_for_cache,
     reshape_and_cache,
@@ -40,6 +41,7 @@ from .paged_attention import (
 
 __all__ = [
     "DTYPES",
+    "copy_blocks",
     "decode_attention",
     "e4m3_code_values",
     "e4m3_decode",

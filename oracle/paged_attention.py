@@ -139,3 +139,21 @@ def decode_attention(q, k_cache, v_cache, block_tables, context_lens, scale, num
             weights = np.exp(logits - logits.max())
             out[s, h] = (weights @ values[:, kv, :]) / weights.sum()
     return out
+
+
+def copy_blocks(k_cache, v_cache, src_blocks, dst_blocks) -> None:
+    """Copy-on-write step, in place: block dst[i] becomes a copy of block src[i] in both caches.
+
+    [vLLM-history] §3.2: before a sequence writes into a physical block that
+    other sequences share, the block is copied and the sequence continues in
+    the copy. Destinations must be distinct and disjoint from the sources
+    (the GPU copies run concurrently, so an overlap would have no defined order).
+    """
+    src = np.asarray(src_blocks, dtype=np.int64)
+    dst = np.asarray(dst_blocks, dtype=np.int64)
+    if src.shape != dst.shape:
+        raise ValueError("src and dst must pair up")
+    if len(np.unique(dst)) != len(dst) or np.intersect1d(src, dst).size:
+        raise ValueError("destinations must be distinct and disjoint from the sources")
+    k_cache[dst] = k_cache[src]
+    v_cache[dst] = v_cache[src]

@@ -18,10 +18,12 @@ LIB_PATH = os.environ.get("PA_LIB", os.path.join(_PKG, "libpa.so"))
 
 PA_DTYPE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2, torch.float8_e4m3fn: 3}
 STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_DTYPE", 3: "PA_ERR_SHAPE", 4: "PA_ERR_UNSUPPORTED",
-          5: "PA_ERR_WORKSPACE", 6: "PA_ERR_LAUNCH"}
+          5: "PA_ERR_WORKSPACE", 6: "PA_ERR_LAUNCH", 7: "PA_ERR_CAPACITY", 8: "PA_ERR_STATE"}
 
 EXPORTS = ("pa_reshape_and_cache", "pa_decode", "pa_decode_split", "pa_decode_workspace_bytes",
-           "pa_decode_partition_blocks", "pa_last_error", "pa_version")
+           "pa_decode_partition_blocks", "pa_copy_blocks", "pa_bm_create", "pa_bm_destroy", "pa_bm_num_free_blocks",
+           "pa_bm_block_refcount", "pa_bm_add_sequence", "pa_bm_fork", "pa_bm_free_sequence", "pa_bm_append_slots",
+           "pa_bm_block_tables", "pa_last_error", "pa_version")
 
 _lock = threading.Lock()
 _lib = None
@@ -58,6 +60,25 @@ def load(path: str | None = None) -> ctypes.CDLL:
         lib.pa_decode_workspace_bytes.restype = _sz
         lib.pa_decode_partition_blocks.argtypes = [_i32] * 6
         lib.pa_decode_partition_blocks.restype = _i32
+        lib.pa_copy_blocks.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _i32, _vp]
+        lib.pa_copy_blocks.restype = _i32
+        lib.pa_bm_create.argtypes = [_i64, _i32, _i32]
+        lib.pa_bm_create.restype = _vp
+        lib.pa_bm_destroy.argtypes = [_vp]
+        lib.pa_bm_destroy.restype = None
+        lib.pa_bm_num_free_blocks.argtypes = [_vp]
+        lib.pa_bm_num_free_blocks.restype = _i64
+        lib.pa_bm_block_refcount.argtypes = [_vp, _i32]
+        lib.pa_bm_block_refcount.restype = _i32
+        for name in ("pa_bm_add_sequence", "pa_bm_free_sequence"):
+            getattr(lib, name).argtypes = [_vp, _i64]
+            getattr(lib, name).restype = _i32
+        lib.pa_bm_fork.argtypes = [_vp, _i64, _i64]
+        lib.pa_bm_fork.restype = _i32
+        lib.pa_bm_append_slots.argtypes = [_vp, _vp, _i32, _vp, _vp, _vp, ctypes.POINTER(_i32)]
+        lib.pa_bm_append_slots.restype = _i32
+        lib.pa_bm_block_tables.argtypes = [_vp, _vp, _i32, _vp, _i32, _vp]
+        lib.pa_bm_block_tables.restype = _i32
         lib.pa_last_error.argtypes = []
         lib.pa_last_error.restype = ctypes.c_char_p
         lib.pa_version.argtypes = []
@@ -171,3 +192,81 @@ def decode(out, q, k_cache, v_cache, block_tables, context_lens, scale: float, n
         num_kv_heads, block_size, S, H, D, M, N, _dtype(q), _dtype(k_cache), _dtype(out), float(k_scale),
         float(v_scale), int(partition_blocks), ws_ptr, ws_bytes, _stream(q, stream)))
     return out
+
+
+def copy_blocks(k_cache, v_cache, src_blocks, dst_blocks, stream=None) -> None:
+    """Copy physical blocks src_blocks[i] -> dst_blocks[i] (int32 device tensors) in both caches."""
+    lib = load()
+    for t in (k_cache, v_cache, src_blocks, dst_blocks):
+        _need(t.is_cuda and t.is_contiguous(), "all tensors must be contiguous device tensors")
+    _need(k_cache.dim() == 4 and v_cache.shape == k_cache.shape and k_cache.dtype == v_cache.dtype,
+          "caches must be [N, Hkv, B, D] of one shape and dtype")
+    _need(src_blocks.dtype == torch.int32 and dst_blocks.dtype == torch.int32 and src_blocks.dim() == 1
+          and dst_blocks.shape == src_blocks.shape, "src/dst blocks must be int32 [n] of one shape")
+    N, Hkv, B, D = k_cache.shape
+    _check(lib, lib.pa_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(src_blocks), _ptr(dst_blocks),
+                                   src_blocks.shape[0], N, Hkv, D, B, _dtype(k_cache), _stream(k_cache, stream)))
+
+
+class BlockManager:
+    """Host-side block pool bookkeeping (pa_bm_* in include/pa.h): free list, sharing, copy-on-write."""
+
+    def __init__(self, num_blocks: int, max_blocks_per_seq: int, block_size: int = 16):
+        self._lib = load()
+        self._h = self._lib.pa_bm_create(num_blocks, block_size, max_blocks_per_seq)
+        if not self._h:
+            raise PAError(3, self._lib.pa_last_error().decode())
+        self.num_blocks = num_blocks
+        self.max_blocks_per_seq = max_blocks_per_seq
+        self.block_size = block_size
+
+    def close(self):
+        if self._h:
+            self._lib.pa_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def num_free_blocks(self) -> int:
+        return int(self._lib.pa_bm_num_free_blocks(self._h))
+
+    def refcount(self, block: int) -> int:
+        return int(self._lib.pa_bm_block_refcount(self._h, block))
+
+    def add_sequence(self, seq_id: int) -> None:
+        _check(self._lib, self._lib.pa_bm_add_sequence(self._h, seq_id))
+
+    def fork(self, parent: int, child: int) -> None:
+        _check(self._lib, self._lib.pa_bm_fork(self._h, parent, child))
+
+    def free_sequence(self, seq_id: int) -> None:
+        _check(self._lib, self._lib.pa_bm_free_sequence(self._h, seq_id))
+
+    def append_slots(self, seq_ids):
+        """One new token per sequence: returns (slots int64 [n], cow_src int32 [k], cow_dst int32 [k]) as numpy."""
+        import numpy as np
+        ids = np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int64))
+        n = len(ids)
+        slots = np.empty(n, np.int64)
+        src = np.empty(max(n, 1), np.int32)
+        dst = np.empty(max(n, 1), np.int32)
+        k = _i32(0)
+        _check(self._lib, self._lib.pa_bm_append_slots(self._h, ids.ctypes.data, n, slots.ctypes.data,
+                                                       src.ctypes.data, dst.ctypes.data, ctypes.byref(k)))
+        return slots, src[:k.value].copy(), dst[:k.value].copy()
+
+    def block_tables(self, seq_ids, max_blocks: int | None = None):
+        """Dense int32 tables [n, max_blocks] (-1 padded) and int32 lengths [n], as numpy."""
+        import numpy as np
+        ids = np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int64))
+        m = max_blocks or self.max_blocks_per_seq
+        tables = np.empty((len(ids), m), np.int32)
+        lens = np.empty(len(ids), np.int32)
+        _check(self._lib, self._lib.pa_bm_block_tables(self._h, ids.ctypes.data, len(ids), tables.ctypes.data, m,
+                                                       lens.ctypes.data))
+        return tables, lens

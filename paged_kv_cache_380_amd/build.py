@@ -2,8 +2,9 @@
 
     python -m paged_kv_cache_380_amd.build [--verbose]
 
-Every ``csrc/*.hip`` file is compiled to an object under ``_build/`` (in
-parallel) and the objects are linked into ``paged_kv_cache_380_amd/libpa.so``.
+Every ``csrc/*.hip`` file is compiled with hipcc and every host-only
+``csrc/*.cpp`` file with the host C++ compiler to an object under ``_build/``
+(in parallel); the objects are linked into ``paged_kv_cache_380_amd/libpa.so``.
 The build always recompiles. Packed-FP32 instruction selection is turned off
 for all device code.
 """
@@ -39,6 +40,13 @@ FILE_FLAGS = {
 }
 
 
+CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+
+
+def cxx() -> str:
+    return os.environ.get("CXX") or shutil.which("g++") or "c++"
+
+
 def hipcc() -> str:
     path = os.environ.get("HIPCC") or shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(path):
@@ -63,11 +71,13 @@ def build(verbose: bool = False, extra_flags=()) -> str:
     os.makedirs(BUILD, exist_ok=True)
     cc = hipcc()
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    objs = [os.path.join(BUILD, os.path.basename(s)[:-4] + ".o") for s in srcs]
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        futs = [ex.submit(_run, [cc, *HIPCC_FLAGS, *FILE_FLAGS.get(os.path.basename(s), []), *extra_flags,
-                                 "-c", s, "-o", o], verbose)
-                for s, o in zip(srcs, objs)]
+    host_srcs = sorted(glob.glob(os.path.join(CSRC, "*.cpp")))  # host-only C++ (no device code)
+    objs = [os.path.join(BUILD, os.path.basename(s).rsplit(".", 1)[0] + ".o") for s in srcs + host_srcs]
+    cmds = [[cc, *HIPCC_FLAGS, *FILE_FLAGS.get(os.path.basename(s), []), *extra_flags, "-c", s, "-o", o]
+            for s, o in zip(srcs, objs)]
+    cmds += [[cxx(), *CXX_FLAGS, "-c", s, "-o", o] for s, o in zip(host_srcs, objs[len(srcs):])]
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(cmds))) as ex:
+        futs = [ex.submit(_run, c, verbose) for c in cmds]
         for f in futs:
             f.result()
     tmp = LIB + ".tmp"

@@ -2,33 +2,19 @@
 // validation on the host, partition and workspace sizing, kernel dispatch.
 // Nothing here reads device memory, allocates or synchronises.
 #include <cmath>
-#include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <string>
 
 #include "pa.h"
+#include "pa_error.h"
 #include "pa_internal.h"
 
 namespace {
 
-thread_local std::string g_last_error;
-
-int fail(int code, const char* fmt, ...) {
-  char buf[512];
-  va_list ap;
-  va_start(ap, fmt);
-  std::vsnprintf(buf, sizeof(buf), fmt, ap);
-  va_end(ap);
-  g_last_error = buf;
-  return code;
-}
-
-int ok() {
-  g_last_error.clear();
-  return PA_OK;
-}
+using pa::fail;
+using pa::ok;
 
 bool activation_kind(int k) { return k == PA_DTYPE_F32 || k == PA_DTYPE_F16 || k == PA_DTYPE_BF16; }
 
@@ -100,8 +86,6 @@ Layout workspace_layout(int num_seqs, int num_heads, int head_size, int max_bloc
 
 extern "C" {
 
-const char* pa_last_error(void) { return g_last_error.c_str(); }
-
 const char* pa_version(void) { return "0.1.0"; }
 
 int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
@@ -130,6 +114,27 @@ int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void
                     slot_is_int64 ? 1 : 0, k_scale, v_scale};
   const hipError_t e = pa::launch_reshape(a, kv_dtype, cache_dtype, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "reshape_and_cache: launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_blocks, const int32_t* dst_blocks, int num_pairs,
+                   int64_t num_blocks, int num_kv_heads, int head_size, int block_size, pa_dtype cache_dtype,
+                   void* stream) {
+  if (num_pairs < 0 || num_pairs > 65535 || num_kv_heads < 1 || num_blocks < 1)
+    return fail(PA_ERR_SHAPE, "copy_blocks: bad sizes (num_pairs=%d in [0,65535], num_kv_heads=%d, num_blocks=%lld)",
+                num_pairs, num_kv_heads, (long long)num_blocks);
+  if (block_size != 16) return fail(PA_ERR_UNSUPPORTED, "copy_blocks: block_size must be 16 (got %d)", block_size);
+  if (head_size != 64 && head_size != 128)
+    return fail(PA_ERR_UNSUPPORTED, "copy_blocks: head_size must be 64 or 128 (got %d)", head_size);
+  if (cache_dtype < PA_DTYPE_F32 || cache_dtype > PA_DTYPE_FP8_E4M3)
+    return fail(PA_ERR_DTYPE, "copy_blocks: unknown cache dtype %d", (int)cache_dtype);
+  if (num_pairs == 0) return ok();
+  if (!k_cache || !v_cache || !src_blocks || !dst_blocks) return fail(PA_ERR_NULL, "copy_blocks: NULL pointer argument");
+  static const int kBytes[] = {4, 2, 2, 1};
+  const int64_t block_bytes = (int64_t)num_kv_heads * block_size * head_size * kBytes[cache_dtype];
+  const hipError_t e = pa::launch_copy_blocks(k_cache, v_cache, src_blocks, dst_blocks, num_pairs, block_bytes,
+                                              num_blocks, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "copy_blocks: launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 

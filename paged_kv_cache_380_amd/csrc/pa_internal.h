@@ -62,6 +62,10 @@ inline int group_tile_for(int group) {
   return 1;
 }
 
+// Copies whole (all KV heads) blocks src[i] -> dst[i] in both caches.
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* src, const int32_t* dst, int num_pairs,
+                              int64_t block_bytes, int64_t num_blocks, hipStream_t stream);
+
 // Query-head tile of the matrix-core kernel (16, 8 or 4 dividing the group), or 0 if none does.
 inline int mfma_group_tile(int group) {
   for (int t = 16; t >= 4; t /= 2)

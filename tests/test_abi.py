@@ -97,6 +97,26 @@ def test_decode_split_rejects_partition(lib, pb):
     assert decode(lib, split=pb) == 4
 
 
+def copy(lib, **kw):
+    a = dict(kc=FAKE, vc=FAKE, src=FAKE, dst=FAKE, n=3, N=64, Hkv=2, D=128, B=16, cd=1, stream=None)
+    a.update(kw)
+    return lib.pa_copy_blocks(a["kc"], a["vc"], a["src"], a["dst"], a["n"], a["N"], a["Hkv"], a["D"], a["B"],
+                              a["cd"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=8), 4), (dict(D=96), 4), (dict(n=-1), 3), (dict(n=70000), 3), (dict(N=0), 3), (dict(Hkv=0), 3),
+    (dict(cd=7), 2), (dict(kc=None), 1), (dict(dst=None), 1),
+])
+def test_copy_blocks_rejects(lib, kw, code):
+    assert copy(lib, **kw) == code
+    assert lib.pa_last_error().decode()
+
+
+def test_copy_blocks_zero_pairs_is_a_no_op(lib):
+    assert copy(lib, n=0, kc=None, src=None) == 0
+
+
 def test_workspace_checks(lib):
     # 4 seqs x 2 KV heads = 8 tiles -> split; a workspace is required
     need = lib.pa_decode_workspace_bytes(4, 8, 2, 128, 64, 16, 0)

@@ -251,6 +251,32 @@ def pin_reshape_locality(O, dtype="f16", cache_dtype=None):
     assert not np.array_equal(kc[touched].view(np.uint8), kc0[touched].view(np.uint8))
 
 
+def pin_copy_blocks(O, dtype="f16", cache_dtype=None):
+    """P12: copy-on-write. After copying a sequence's blocks to free blocks and
+    pointing its table at the copies, decode gives bitwise the same output; no
+    other block changes."""
+    w = small(seed=14, dtype=dtype, cache=cache_dtype, lens=(21, 40, 7))
+    kc, vc = filled(O, w)
+    out0 = run_decode(O, w, kc, vc)
+    tables = w.block_tables.numpy().copy()
+    used = np.unique(tables[tables >= 0])
+    free = np.setdiff1d(np.arange(w.num_blocks), used)
+    src = tables[1][tables[1] >= 0]
+    dst = free[:len(src)]
+    kc0, vc0 = kc.copy(), vc.copy()
+    O.copy_blocks(kc, vc, src, dst)
+    others = np.setdiff1d(np.arange(w.num_blocks), dst)
+    assert np.array_equal(kc[others].view(np.uint8), kc0[others].view(np.uint8))
+    assert np.array_equal(vc[others].view(np.uint8), vc0[others].view(np.uint8))
+    tables[1][tables[1] >= 0] = dst
+    kc[src] = kc0[free[-1]]  # the originals no longer back sequence 1: make them differ
+    vc[src] = vc0[free[-1]]
+    out1 = run_decode(O, w, kc, vc, tables=tables)
+    assert np.array_equal(out0[1], out1[1])
+    with pytest.raises(ValueError):
+        O.copy_blocks(kc, vc, [1, 2], [2, 3])
+
+
 def pin_e4m3_golden(O):
     """P11a: the code table holds the code points printed in the OCP OFP8 specification."""
     vals = O.e4m3_code_values()
@@ -382,6 +408,11 @@ def test_p10_reshape_locality(dtype, cache):
     pin_reshape_locality(oracle, dtype, cache)
 
 
+@pytest.mark.parametrize("dtype,cache", [("f16", None), ("bf16", "fp8_e4m3"), ("f32", None)])
+def test_p12_copy_blocks(dtype, cache):
+    pin_copy_blocks(oracle, dtype, cache)
+
+
 def test_p11_e4m3():
     pin_e4m3_golden(oracle)
     pin_e4m3_nearest_even(oracle)
@@ -412,6 +443,8 @@ MUTANTS = {
     "e4m3 bias 8": ("2.0 ** (exp_field - 7)", "2.0 ** (exp_field - 8)"),
     "e4m3 round half up": ("mag = np.rint(a / quantum) * quantum", "mag = np.floor(a / quantum + 0.5) * quantum"),
     "e4m3 no saturation": ("mag = np.where(a > E4M3_MAX, E4M3_MAX, mag)", "mag = np.where(a > E4M3_MAX, 0.0, mag)"),
+    "copy: V not copied": ("v_cache[dst] = v_cache[src]", "v_cache[dst] = v_cache[dst]"),
+    "copy: direction reversed": ("k_cache[dst] = k_cache[src]", "k_cache[src] = k_cache[dst]"),
 }
 
 
@@ -432,6 +465,7 @@ def _mutant(find: str, repl: str) -> types.SimpleNamespace:
     exec(compile(src_p, "mut_pa", "exec"), p.__dict__)
     return types.SimpleNamespace(
         decode_attention=p.decode_attention, reshape_and_cache=p.reshape_and_cache, widen=p.widen,
+        copy_blocks=p.copy_blocks,
         e4m3_code_values=e.e4m3_code_values, e4m3_encode=e.e4m3_encode, e4m3_decode=e.e4m3_decode)
 
 
@@ -442,7 +476,7 @@ def _runs_clean(O) -> bool:
         lambda: pin_equal_keys_give_mean(O), lambda: pin_two_token_closed_form(O), lambda: pin_brute_force(O),
         lambda: pin_gqa_equals_repeated_mha(O), lambda: pin_reshape_round_trip(O),
         lambda: pin_reshape_locality(O), lambda: pin_e4m3_golden(O), lambda: pin_e4m3_vs_torch(O),
-        lambda: pin_fp8_cache_quantisation(O),
+        lambda: pin_fp8_cache_quantisation(O), lambda: pin_copy_blocks(O),
     ]
     for v in variants:
         try:
