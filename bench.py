@@ -217,6 +217,9 @@ def main():
                     metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR", "COPY_MIB", "OUT"),
                     help="write the HBM-traffic summary of rocprofv3 --pmc runs for --workload and exit")
     ap.add_argument("--command", action="append", default=[], help="profiling commands recorded in a summary")
+    ap.add_argument("--op", choices=("decode", "prefill", "copy"), default="decode",
+                    help="decode: the decode step (default, the headline); prefill: chunked-prefill attention "
+                         "(TFLOP/s); copy: copy-on-write block copies (GB/s)")
     args = ap.parse_args()
 
     if args.summarize_stats:
@@ -253,6 +256,11 @@ def main():
     binding.load()
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from pa_testlib import GpuCase
+
+    if args.op == "prefill":
+        return bench_prefill(args, dev)
+    if args.op == "copy":
+        return bench_copy(args, dev)
 
     log(f"[bench] building {args.workload}")
     w = wl.named(args.workload, args.seed)
@@ -342,6 +350,95 @@ def main():
         log(f"[bench] oracle sample (~{args.cpu_seconds:.0f} s)")
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(res), flush=True)
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 matrix peak, published
+
+
+def _events_ms(fn, steps: int, stream) -> list:
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return sorted(a.elapsed_time(b) for a, b in ev)
+
+
+def bench_prefill(args, dev):
+    """Chunked-prefill attention, Llama-3-8B-shaped GQA: 8 prompts of 2048 tokens each as one chunk."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_380_amd import binding
+    from paged_kv_cache_380_amd import workloads as wl
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from pa_testlib import GpuCase
+    S, L, H, Hkv, D = 8, 2048, 32, 8, 128
+    w = wl.build("prefill_llama3_8b_bf16_b8x2048", [L] * S, H, Hkv, D, "bf16", seed=6, free_fraction=0.05)
+    log(f"[bench] building {w.name}")
+    case = GpuCase(w, device=dev)
+    case.append()
+    g = torch.Generator().manual_seed(7)
+    q = torch.randn((S * L, H, D), generator=g).to(torch.bfloat16).to(dev)
+    out = torch.empty_like(q)
+    starts = torch.arange(0, S * L + 1, L, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    run = lambda: binding.prefill(out, q, case.kc, case.vc, case.tables, case.lens, starts, w.scale, Hkv, L)
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        run()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    durs = _events_ms(run, args.steps, stream)
+    k_ms = sum(durs) / len(durs)
+    pairs = S * L * (L + 1) // 2                       # (query, key) pairs under the causal mask, per head
+    flops = 4.0 * D * H * pairs                        # q.k and p.v, 2 flops per multiply-add
+    tflops = flops / (k_ms * 1e-3) / 1e12
+    print(json.dumps({
+        "metric": "paged chunked-prefill attention TFLOP/s (algorithmic, causal)", "value": round(tflops, 1),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "num_seqs": S, "prompt_tokens": L, "num_heads": H, "num_kv_heads": Hkv,
+                   "head_size": D, "block_size": 16},
+        "roofline": {"kernel": "prefill_mfma", "bound": "mfma", "achieved": round(tflops, 1),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "algorithmic_flops_per_launch": flops},
+        "kernel_ms": round(k_ms, 5),
+    }), flush=True)
+
+
+def bench_copy(args, dev):
+    """Copy-on-write block copies: 512 (source, destination) pairs of Llama-3-8B-shaped bf16 blocks."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_380_amd import binding
+    N, Hkv, D, P = 4096, 8, 128, 512
+    kc = torch.randn((N, Hkv, 16, D), device=dev).to(torch.bfloat16)
+    vc = torch.randn((N, Hkv, 16, D), device=dev).to(torch.bfloat16)
+    perm = np.random.default_rng(8).permutation(N)
+    src = torch.from_numpy(perm[:P].astype(np.int32)).to(dev)
+    dst = torch.from_numpy(perm[P:2 * P].astype(np.int32)).to(dev)
+    stream = torch.cuda.current_stream(dev)
+    run = lambda: binding.copy_blocks(kc, vc, src, dst)
+    for _ in range(args.warmup):
+        run()
+    durs = _events_ms(run, args.steps, stream)
+    k_ms = sum(durs) / len(durs)
+    moved = 2 * 2 * P * Hkv * 16 * D * 2               # K and V, read + write
+    gbs = moved / (k_ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "copy-on-write block copies GB/s (read + write)", "value": round(gbs, 1), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(k_ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "copy_blocks_512_pairs_bf16", "pairs": P, "num_kv_heads": Hkv, "head_size": D},
+        "roofline": {"kernel": "copy_blocks_kernel", "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": moved},
+    }), flush=True)
 
 
 def decode_kernel(w) -> str:

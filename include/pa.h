@@ -151,6 +151,39 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
               size_t workspace_bytes, void* stream);
 
 /*
+ * pa_prefill -- chunked-prefill attention over the paged cache ("vLLM 前世今生"
+ * §5.4 and §7.3: a long prompt is processed in chunks that run next to
+ * decode steps; §3.2: the paged cache).
+ *
+ * Sequence s has context_lens[s] tokens in the cache, the last
+ * q_len = query_start_loc[s+1] - query_start_loc[s] of which are its current
+ * chunk (their K/V written with pa_reshape_and_cache beforehand). Query row
+ * t = query_start_loc[s] + i (i < q_len) sits at position
+ * p = context_lens[s] - q_len + i and attends causally to positions 0..p:
+ *   out[t, h, :] = sum_{j<=p} w_j V_j / sum_{j<=p} w_j,  w_j = exp(scale * dot(q[t, h], K_j)),
+ * with K_j, V_j read through the block table as in pa_decode (FP8 codes times
+ * k_scale / v_scale). A chunk of one token is a decode step.
+ *
+ *   out             device, [num_tokens, num_heads, head_size], out_dtype (q_dtype or F32)
+ *   q               device, [num_tokens, num_heads, head_size], F16 or BF16
+ *   k_cache, v_cache device, as in pa_decode; cache_dtype == q_dtype or FP8_E4M3
+ *   block_tables    device, int32 [num_seqs, max_blocks_per_seq]
+ *   context_lens    device, int32 [num_seqs] (chunk included)
+ *   query_start_loc device, int32 [num_seqs + 1], non-decreasing, starting at 0
+ *   max_query_len   host upper bound of every q_len (sizes the grid)
+ *
+ * A q_len above max_query_len or above context_lens[s] is cut to the smaller
+ * bound; rows beyond it are not written. Accumulation is float32 (weights
+ * carried as two 16-bit parts); results agree with the definition within
+ * float32 accumulation error. Runs on the matrix cores; no workspace.
+ */
+int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+               const int32_t* context_lens, const int32_t* query_start_loc, float scale, int num_kv_heads,
+               int block_size, int num_seqs, int num_heads, int head_size, int max_blocks_per_seq,
+               int64_t num_blocks, int max_query_len, pa_dtype q_dtype, pa_dtype cache_dtype, pa_dtype out_dtype,
+               float k_scale, float v_scale, void* stream);
+
+/*
  * pa_decode_split -- pa_decode with an explicit partition length.
  *
  * partition_blocks = number of 16-token blocks per partition, a multiple of 4

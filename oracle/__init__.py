@@ -34,6 +34,7 @@ from .paged_attention import (
     DTYPES,
     copy_blocks,
     decode_attention,
+    prefill_attention,
     quantize_for_cache,
     reshape_and_cache,
     widen,
@@ -43,6 +44,7 @@ __all__ = [
     "DTYPES",
     "copy_blocks",
     "decode_attention",
+    "prefill_attention",
     "e4m3_code_values",
     "e4m3_decode",
     "e4m3_encode",

@@ -157,3 +157,49 @@ def copy_blocks(k_cache, v_cache, src_blocks, dst_blocks) -> None:
         raise ValueError("destinations must be distinct and disjoint from the sources")
     k_cache[dst] = k_cache[src]
     v_cache[dst] = v_cache[src]
+
+
+def prefill_attention(q, k_cache, v_cache, block_tables, context_lens, query_start_loc, scale, num_kv_heads,
+                      block_size, q_dtype, cache_dtype, k_scale=1.0, v_scale=1.0) -> np.ndarray:
+    """Chunked-prefill attention over a paged cache, in float64. Returns [num_tokens, num_heads, head_size].
+
+    [vLLM-history] §5.4 and §7.3 (chunked prefill: a long prompt is cut into
+    chunks that run next to decode steps). Sequence s contributes the query
+    rows query_start_loc[s] .. query_start_loc[s+1]-1, the last q_len of its
+    context_lens[s] tokens, whose K and V are already in the cache. Query i of
+    the chunk sits at position p = context_lens[s] - q_len + i and attends to
+    the cached tokens 0..p (causal), reached through the block table as in
+    decode_attention: softmax(K q . scale) weighted V over those tokens.
+    """
+    q = np.asarray(q)
+    T, H, D = q.shape
+    if H % num_kv_heads:
+        raise ValueError("num_heads must be a multiple of num_kv_heads")
+    starts = np.asarray(query_start_loc, dtype=np.int64)
+    group = H // num_kv_heads
+    scale64 = float(np.float32(scale))
+    k_scale = k_scale if cache_dtype == "fp8_e4m3" else 1.0
+    v_scale = v_scale if cache_dtype == "fp8_e4m3" else 1.0
+    out = np.zeros((T, H, D), dtype=np.float64)
+    for s in range(len(starts) - 1):
+        q0, q1 = int(starts[s]), int(starts[s + 1])
+        n = int(context_lens[s])
+        qlen = q1 - q0
+        if qlen == 0:
+            continue
+        if qlen > n:
+            raise ValueError("a chunk cannot be longer than its context")
+        pos = np.arange(n)
+        phys = np.asarray(block_tables[s], dtype=np.int64)[pos // block_size]
+        rows = pos % block_size
+        keys = widen(k_cache[phys, :, rows, :], cache_dtype, k_scale)    # [n, num_kv_heads, D]
+        values = widen(v_cache[phys, :, rows, :], cache_dtype, v_scale)
+        for i in range(qlen):
+            p = n - qlen + i                                             # this query's position
+            qs = widen(q[q0 + i], q_dtype)                               # [H, D]
+            for h in range(H):
+                kv = h // group
+                logits = scale64 * (keys[:p + 1, kv, :] @ qs[h])
+                weights = np.exp(logits - logits.max())
+                out[q0 + i, h] = (weights @ values[:p + 1, kv, :]) / weights.sum()
+    return out

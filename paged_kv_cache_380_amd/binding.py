@@ -21,7 +21,7 @@ STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_DTYPE", 3: "PA_ERR_SHAPE", 4:
           5: "PA_ERR_WORKSPACE", 6: "PA_ERR_LAUNCH", 7: "PA_ERR_CAPACITY", 8: "PA_ERR_STATE"}
 
 EXPORTS = ("pa_reshape_and_cache", "pa_decode", "pa_decode_split", "pa_decode_workspace_bytes",
-           "pa_decode_partition_blocks", "pa_copy_blocks", "pa_bm_create", "pa_bm_destroy", "pa_bm_num_free_blocks",
+           "pa_decode_partition_blocks", "pa_prefill", "pa_copy_blocks", "pa_bm_create", "pa_bm_destroy", "pa_bm_num_free_blocks",
            "pa_bm_block_refcount", "pa_bm_add_sequence", "pa_bm_fork", "pa_bm_free_sequence", "pa_bm_append_slots",
            "pa_bm_block_tables", "pa_last_error", "pa_version")
 
@@ -60,6 +60,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
         lib.pa_decode_workspace_bytes.restype = _sz
         lib.pa_decode_partition_blocks.argtypes = [_i32] * 6
         lib.pa_decode_partition_blocks.restype = _i32
+        lib.pa_prefill.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _i32, _i32, _i32, _i32, _i32, _i32, _i64,
+                                   _i32, _i32, _i32, _i32, _f32, _f32, _vp]
+        lib.pa_prefill.restype = _i32
         lib.pa_copy_blocks.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _i32, _vp]
         lib.pa_copy_blocks.restype = _i32
         lib.pa_bm_create.argtypes = [_i64, _i32, _i32]
@@ -270,3 +273,29 @@ class BlockManager:
         _check(self._lib, self._lib.pa_bm_block_tables(self._h, ids.ctypes.data, len(ids), tables.ctypes.data, m,
                                                        lens.ctypes.data))
         return tables, lens
+
+
+def prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc, scale: float, num_kv_heads: int,
+            max_query_len: int, block_size: int = 16, k_scale: float = 1.0, v_scale: float = 1.0,
+            stream=None) -> torch.Tensor:
+    """Chunked-prefill attention: q/out [T, H, D]; query_start_loc int32 [S+1]; causal within each chunk."""
+    lib = load()
+    for t in (out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc):
+        _need(t.is_cuda and t.is_contiguous(), "all tensors must be contiguous device tensors")
+    _need(q.dim() == 3 and out.shape == q.shape, "q/out must be [T, H, D] of one shape")
+    _need(k_cache.dim() == 4 and v_cache.shape == k_cache.shape and k_cache.dtype == v_cache.dtype,
+          "caches must be [N, Hkv, B, D] of one shape and dtype")
+    _need(block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32
+          and query_start_loc.dtype == torch.int32, "tables, lengths and query_start_loc must be int32")
+    S = context_lens.shape[0]
+    _need(block_tables.dim() == 2 and block_tables.shape[0] == S and query_start_loc.shape == (S + 1,),
+          "block_tables must be [S, M] and query_start_loc [S + 1]")
+    T, H, D = q.shape
+    N, Hkv, B, D2 = k_cache.shape
+    _need(Hkv == num_kv_heads and B == block_size and D2 == D, "cache shape does not match the arguments")
+    _check(lib, lib.pa_prefill(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+        _ptr(query_start_loc), float(scale), num_kv_heads, block_size, S, H, D, block_tables.shape[1], N,
+        int(max_query_len), _dtype(q), _dtype(k_cache), _dtype(out), float(k_scale), float(v_scale),
+        _stream(q, stream)))
+    return out

@@ -37,6 +37,7 @@ HIPCC_FLAGS = [
 # accumulators out of and back into AGPRs on every block.
 FILE_FLAGS = {
     "pa_decode_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "pa_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

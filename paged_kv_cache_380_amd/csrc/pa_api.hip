@@ -138,6 +138,66 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_blocks, cons
   return ok();
 }
 
+int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+               const int32_t* context_lens, const int32_t* query_start_loc, float scale, int num_kv_heads,
+               int block_size, int num_seqs, int num_heads, int head_size, int max_blocks_per_seq,
+               int64_t num_blocks, int max_query_len, pa_dtype q_dtype, pa_dtype cache_dtype, pa_dtype out_dtype,
+               float k_scale, float v_scale, void* stream) {
+  if (block_size != 16) return fail(PA_ERR_UNSUPPORTED, "prefill: block_size must be 16 (got %d)", block_size);
+  if (head_size != 64 && head_size != 128)
+    return fail(PA_ERR_UNSUPPORTED, "prefill: head_size must be 64 or 128 (got %d)", head_size);
+  if (num_seqs < 0 || num_seqs > 65535 || num_heads < 1 || num_kv_heads < 1 || max_blocks_per_seq < 1 ||
+      num_blocks < 1 || max_query_len < 0)
+    return fail(PA_ERR_SHAPE,
+                "prefill: bad sizes (num_seqs=%d in [0,65535], num_heads=%d, num_kv_heads=%d, "
+                "max_blocks_per_seq=%d, num_blocks=%lld, max_query_len=%d)",
+                num_seqs, num_heads, num_kv_heads, max_blocks_per_seq, (long long)num_blocks, max_query_len);
+  if (num_heads % num_kv_heads)
+    return fail(PA_ERR_SHAPE, "prefill: num_heads (%d) is not a multiple of num_kv_heads (%d)", num_heads,
+                num_kv_heads);
+  if (q_dtype != PA_DTYPE_F16 && q_dtype != PA_DTYPE_BF16)
+    return fail(PA_ERR_DTYPE, "prefill: q dtype must be F16 or BF16 (matrix-core kernel)");
+  const bool fp8 = cache_dtype == PA_DTYPE_FP8_E4M3;
+  if (!(cache_dtype == q_dtype || fp8))
+    return fail(PA_ERR_DTYPE, "prefill: cache dtype must equal the q dtype or be FP8_E4M3");
+  if (out_dtype != q_dtype && out_dtype != PA_DTYPE_F32)
+    return fail(PA_ERR_DTYPE, "prefill: out dtype must be the q dtype or F32");
+  if (!std::isfinite(scale)) return fail(PA_ERR_SHAPE, "prefill: scale must be finite");
+  if (fp8 && !(std::isfinite(k_scale) && std::isfinite(v_scale) && k_scale > 0.f && v_scale > 0.f))
+    return fail(PA_ERR_SHAPE, "prefill: FP8 scales must be finite and positive");
+  const int64_t group = num_heads / num_kv_heads;
+  const int64_t row_tiles = ((int64_t)max_query_len * group + 63) / 64;
+  if (row_tiles * num_kv_heads > 0x7fffffffLL)
+    return fail(PA_ERR_UNSUPPORTED, "prefill: max_query_len %d too large", max_query_len);
+  if (num_seqs == 0 || max_query_len == 0) return ok();
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start_loc)
+    return fail(PA_ERR_NULL, "prefill: NULL pointer argument");
+  pa::PrefillArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.query_start_loc = query_start_loc;
+  const double log2e = 1.4426950408889634;
+  a.qk_scale = (float)((double)scale * log2e * (fp8 ? (double)k_scale : 1.0));
+  a.out_scale = fp8 ? v_scale : 1.0f;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_size = head_size;
+  a.group = (int)group;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.row_tiles = (int)row_tiles;
+  a.max_query_len = max_query_len;
+  a.out_kind = out_dtype;
+  const hipError_t e = pa::launch_prefill(a, q_dtype, cache_dtype, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "prefill: launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 int pa_decode_partition_blocks(int num_seqs, int num_heads, int num_kv_heads, int head_size,
                                int max_blocks_per_seq, int block_size) {
   if (!shapes_ok(num_seqs, num_heads, num_kv_heads, head_size, max_blocks_per_seq, block_size)) return 0;

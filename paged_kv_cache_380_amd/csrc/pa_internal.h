@@ -62,6 +62,30 @@ inline int group_tile_for(int group) {
   return 1;
 }
 
+struct PrefillArgs {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* query_start_loc;  // [num_seqs + 1]
+  float qk_scale;         // scale * log2(e) (* k_scale for FP8 caches)
+  float out_scale;        // v_scale for FP8 caches, else 1
+  int num_seqs;
+  int num_heads;
+  int num_kv_heads;
+  int head_size;
+  int group;
+  int max_blocks;
+  int64_t num_blocks;
+  int row_tiles;          // workgroups per KV head and sequence: ceil(max_query_len * group / 64)
+  int max_query_len;      // rows of longer chunks past this many tokens are not computed
+  int out_kind;
+};
+
+hipError_t launch_prefill(const PrefillArgs& a, int q_kind, int cache_kind, hipStream_t stream);
+
 // Copies whole (all KV heads) blocks src[i] -> dst[i] in both caches.
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* src, const int32_t* dst, int num_pairs,
                               int64_t block_bytes, int64_t num_blocks, hipStream_t stream);

@@ -1,0 +1,269 @@
+// Chunked-prefill attention over the paged cache, on the gfx950 matrix cores.
+//
+// What is computed ("vLLM 前世今生" §5.4 and §7.3, chunked prefill; §3.2, the
+// paged cache): a sequence's chunk of q_len new query tokens, the last q_len
+// of its context_len tokens (whose K/V are already in the cache), attends
+// causally: query i of the chunk, at position p = context_len - q_len + i,
+// sees the tokens 0..p, reached through the sequence's block table. Per query
+// head: softmax(q·Kᵀ·scale)·V over those tokens.
+//
+// How: this is the dense, compute-bound side of paged attention, so it runs
+// as MFMA tiles, flash-attention style (online softmax over key blocks):
+//  * the (token, head) pairs of one KV head form the rows of the problem;
+//    a workgroup of 4 waves takes 64 consecutive rows (row = token * G + head
+//    within the group, so grouped heads share every K/V tile), 16 per wave;
+//  * the workgroup streams the sequence's 16-token blocks up to the last
+//    position among its rows. Each block's K and V tile is loaded once, by all
+//    four waves together, into double-buffered LDS (rows padded by 16 bytes
+//    against bank conflicts; FP8 widened exactly to the 16-bit type), while
+//    the waves compute on the previous block;
+//  * per wave and block, S = K·Qᵀ is 16x16x32 MFMAs on K read from LDS in the
+//    A-operand layout; the lane layout of S is the A-operand layout of P, so
+//    the online softmax (a lazily moved per-row reference max) runs in place;
+//    O += P·V is 16x16x16 MFMAs with P split into 16-bit hi + lo and V read
+//    transposed from LDS;
+//  * causality is a per-row limit on the key index, applied by selection; a
+//    wave whose rows all end before a block skips its arithmetic.
+// No split over keys is done: a chunk's rows already give many workgroups.
+#include "pa_decode_common.h"
+#include "pa_mfma.h"
+
+namespace pa {
+namespace {
+
+constexpr int kRows = 64;  // rows (token, head pairs) per workgroup, 16 per wave
+constexpr float kPSlack = 8.0f;
+
+template <int CK, int D> struct PGeo {
+  static constexpr int kBytes = KindBytes<CK>::value;
+  static constexpr int kRowBytes = D * kBytes;
+  static constexpr int kTileBytes = 16 * kRowBytes;
+  static constexpr int NL = kTileBytes / 1024;       // wave-loads of 1 KiB per tile (K or V)
+  static constexpr int NLW = (2 * NL + kWaves - 1) / kWaves;  // loads per wave per block (K and V together)
+  static constexpr int NKB = D / 32;
+  static constexpr int NDB = D / 16;
+  static constexpr int S = D + 8;                    // LDS row stride of a staged tile, 16-bit elements
+};
+
+template <int QK, int CK, int D>
+__global__ __launch_bounds__(kThreads) void prefill_mfma(const PrefillArgs a) {
+  using G = PGeo<CK, D>;
+  constexpr int NL = G::NL, NLW = G::NLW, NKB = G::NKB, NDB = G::NDB, S = G::S;
+  static_assert(QK == kF16 || QK == kBF16, "16-bit queries");
+
+  __shared__ __align__(16) uint16_t s_k[2][16 * S];
+  __shared__ __align__(16) uint16_t s_v[2][16 * S];
+
+  const int kvh = blockIdx.x / a.row_tiles;
+  const int rt = blockIdx.x - kvh * a.row_tiles;
+  const int seq = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15;
+  const int g = lane >> 4;
+
+  const int q0 = a.query_start_loc[seq];
+  const int ctx = min(a.context_lens[seq], a.max_blocks * 16);
+  const int qlen = min(a.query_start_loc[seq + 1] - q0, ctx);  // the chunk: positions ctx - qlen .. ctx - 1
+  const int rows = min(qlen, a.max_query_len) * a.group;        // rows computed (the grid covers max_query_len)
+  const int row0 = rt * kRows;
+  if (row0 >= rows) return;
+  const int last_row = min(row0 + kRows, rows) - 1;
+  const int nblk = (ctx - qlen + last_row / a.group + 1 + 15) >> 4;  // blocks up to the last row's position
+
+  // This lane's S column: row n of the wave's 16.
+  const int my_row = row0 + wave * 16 + n;
+  const bool row_ok = my_row < rows;
+  const int my_tok = row_ok ? my_row / a.group : 0;
+  const int my_head = kvh * a.group + (row_ok ? my_row - my_tok * a.group : 0);
+  const int my_limit = row_ok ? ctx - qlen + my_tok + 1 : 0;  // keys visible to this row
+  // The wave's largest limit (its last valid row): blocks at or past it are skipped.
+  const int wave_last = min(row0 + wave * 16 + 15, rows - 1);
+  const int wave_limit = row0 + wave * 16 < rows ? ctx - qlen + wave_last / a.group + 1 : 0;
+
+  uint32_t qf[NKB][4];
+  {
+    const char* qp = static_cast<const char*>(a.q) + ((int64_t)(q0 + my_tok) * a.num_heads + my_head) * D * 2;
+#pragma unroll
+    for (int b = 0; b < NKB; ++b) {
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (row_ok) v = *reinterpret_cast<const uint4*>(qp + (32 * b + 8 * g) * 2);
+      qf[b][0] = v.x;
+      qf[b][1] = v.y;
+      qf[b][2] = v.z;
+      qf[b][3] = v.w;
+    }
+  }
+
+  const int32_t* bt = a.block_tables + (int64_t)seq * a.max_blocks;
+  const int64_t blk_stride = (int64_t)a.num_kv_heads * G::kTileBytes;
+  const char* kbase = static_cast<const char*>(a.k_cache) + (int64_t)kvh * G::kTileBytes;
+  const char* vbase = static_cast<const char*>(a.v_cache) + (int64_t)kvh * G::kTileBytes;
+
+  // Block j's tiles, as this wave's share of the 2*NL wave-loads (K first, then V).
+  uint4 pre[NLW];
+  auto issue = [&](int j) {
+    const int phys = __builtin_amdgcn_readfirstlane(bt[j]);
+    const int64_t off = ((uint32_t)phys < (uint64_t)a.num_blocks ? phys : 0) * blk_stride;
+#pragma unroll
+    for (int u = 0; u < NLW; ++u) {
+      const int L = wave + u * kWaves;
+      if (L < 2 * NL) {
+        const char* base = L < NL ? kbase : vbase;
+        pre[u] = load_stream(base + off + (L % NL) * 1024 + lane * 16);
+      }
+    }
+  };
+  auto stage = [&](int j, int buf) {
+#pragma unroll
+    for (int u = 0; u < NLW; ++u) {
+      const int L = wave + u * kWaves;
+      if (L < 2 * NL) {
+        const bool is_v = L >= NL;
+        const int byte = (L % NL) * 1024 + lane * 16;
+        const int row = byte / G::kRowBytes;
+        const int col = (byte % G::kRowBytes) / G::kBytes;
+        // rows past the context may hold anything: V rows there become zero
+        // (a zero weight times NaN would still be NaN); K rows are masked later
+        const bool zero = is_v && j * 16 + row >= ctx;
+        uint16_t* dst = (is_v ? s_v[buf] : s_k[buf]) + row * S + col;
+        uint4 v = pre[u];
+        if constexpr (CK == kFP8) {
+          uint4 w0, w1;
+          fp8x4_to_16<QK>(v.x, w0.x, w0.y);
+          fp8x4_to_16<QK>(v.y, w0.z, w0.w);
+          fp8x4_to_16<QK>(v.z, w1.x, w1.y);
+          fp8x4_to_16<QK>(v.w, w1.z, w1.w);
+          if (zero) w0 = w1 = make_uint4(0u, 0u, 0u, 0u);
+          *reinterpret_cast<uint4*>(dst) = w0;
+          *reinterpret_cast<uint4*>(dst + 8) = w1;
+        } else {
+          if (zero) v = make_uint4(0u, 0u, 0u, 0u);
+          *reinterpret_cast<uint4*>(dst) = v;
+        }
+      }
+    }
+  };
+
+  f32x4_t acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  float mref = kNegInf;
+  float lsum = 0.f;
+  const float qk_scale = a.qk_scale;
+
+  auto compute = [&](int j, int buf) {
+    if (j * 16 >= wave_limit) return;  // every row of this wave ends before this block
+    const uint16_t* sk = s_k[buf];
+    const uint16_t* sv = s_v[buf];
+    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int b = 0; b < NKB; ++b) {
+      const uint4 kw = *reinterpret_cast<const uint4*>(sk + n * S + 32 * b + 8 * g);
+      const uint32_t w[4] = {kw.x, kw.y, kw.z, kw.w};
+      s = mma_k32<QK>(w, qf[b], s);
+    }
+    float x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[i] = s[i] * qk_scale;
+      if (j * 16 + 4 * g + i >= my_limit) x[i] = kNegInf;  // causal limit (and rows past the context)
+    }
+    const float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    if (__builtin_amdgcn_ballot_w64(bm > mref + kPSlack) != 0) {
+      float bmx = fmaxf(bm, __shfl_xor(bm, 16, 64));
+      bmx = fmaxf(bmx, __shfl_xor(bmx, 32, 64));
+      const float mn = fmaxf(mref, bmx);
+      const float alpha = fast_exp2(mref - ((mn == kNegInf) ? 0.f : mn));
+      lsum *= alpha;
+      mref = mn;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float al = __shfl(alpha, 4 * g + i, 64);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) acc[db][i] *= al;
+      }
+    }
+    const float ms = (mref == kNegInf) ? 0.f : mref;
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = fast_exp2(x[i] - ms);
+      lsum += p[i];
+    }
+    const uint32_t h01 = pack2<QK>(p[0], p[1]);
+    const uint32_t h23 = pack2<QK>(p[2], p[3]);
+    const uint32_t l01 = pack2<QK>(p[0] - lo16_to_f32<QK>(h01), p[1] - hi16_to_f32<QK>(h01));
+    const uint32_t l23 = pack2<QK>(p[2] - lo16_to_f32<QK>(h23), p[3] - hi16_to_f32<QK>(h23));
+    const uint16_t* vrow = sv + 4 * g * S + n;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const uint32_t b0 = (uint32_t)vrow[db * 16] | ((uint32_t)vrow[S + db * 16] << 16);
+      const uint32_t b1 = (uint32_t)vrow[2 * S + db * 16] | ((uint32_t)vrow[3 * S + db * 16] << 16);
+      acc[db] = mma_k16<QK>(h01, h23, b0, b1, acc[db]);
+      acc[db] = mma_k16<QK>(l01, l23, b0, b1, acc[db]);
+    }
+  };
+
+  issue(0);
+  stage(0, 0);
+  __syncthreads();
+  for (int j = 0; j < nblk; ++j) {
+    const bool more = j + 1 < nblk;
+    if (more) issue(j + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(j, j & 1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (more) stage(j + 1, (j + 1) & 1);
+    __syncthreads();
+  }
+
+  // Normalise and write this wave's rows: lane (n, g) holds rows 4g + i, column 16 db + n.
+  lsum += __shfl_xor(lsum, 16, 64);
+  lsum += __shfl_xor(lsum, 32, 64);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = row0 + wave * 16 + 4 * g + i;
+    const float L = __shfl(lsum, 4 * g + i, 64);
+    if (r < rows) {
+      const int tok = r / a.group;
+      const int head = kvh * a.group + (r - tok * a.group);
+      const int64_t base = ((int64_t)(q0 + tok) * a.num_heads + head) * D;
+      const float inv = L > 0.f ? a.out_scale / L : 0.f;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int64_t e = base + db * 16 + n;
+        const float v = acc[db][i] * inv;
+        if (a.out_kind == kF32) static_cast<float*>(a.out)[e] = v;
+        else if (a.out_kind == kBF16) static_cast<uint16_t*>(a.out)[e] = f32_to_bf16_rne(v);
+        else static_cast<uint16_t*>(a.out)[e] = f32_to_f16_rne(v);
+      }
+    }
+  }
+}
+
+template <int QK, int CK>
+hipError_t launch_d(const PrefillArgs& a, hipStream_t stream) {
+  const dim3 grid((unsigned)(a.row_tiles * a.num_kv_heads), (unsigned)a.num_seqs);
+  switch (a.head_size) {
+    case 64: prefill_mfma<QK, CK, 64><<<grid, dim3(kThreads), 0, stream>>>(a); break;
+    case 128: prefill_mfma<QK, CK, 128><<<grid, dim3(kThreads), 0, stream>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillArgs& a, int q_kind, int cache_kind, hipStream_t stream) {
+  switch (q_kind * 4 + cache_kind) {
+    case kF16 * 4 + kF16: return launch_d<kF16, kF16>(a, stream);
+    case kBF16 * 4 + kBF16: return launch_d<kBF16, kBF16>(a, stream);
+    case kF16 * 4 + kFP8: return launch_d<kF16, kFP8>(a, stream);
+    case kBF16 * 4 + kFP8: return launch_d<kBF16, kFP8>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace pa

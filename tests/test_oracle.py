@@ -277,6 +277,87 @@ def pin_copy_blocks(O, dtype="f16", cache_dtype=None):
         O.copy_blocks(kc, vc, [1, 2], [2, 3])
 
 
+def prefill_case(seed, lens, qlens, H=4, Hkv=2, D=8, dtype="f32", cache=None):
+    """A small batch whose caches hold every context token, plus chunk queries (the last qlens tokens)."""
+    w = small(seed=seed, dtype=dtype, cache=cache, lens=lens, H=H, Hkv=Hkv, D=D)
+    rng = np.random.default_rng(seed)
+    starts = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    q = to_store(rng.standard_normal((int(starts[-1]), H, D)), dtype)
+    return w, q, starts
+
+
+def run_prefill(O, w, kc, vc, q, starts, tables=None, lens=None):
+    return O.prefill_attention(q, kc, vc, w.block_tables.numpy() if tables is None else tables,
+                               w.context_lens.numpy() if lens is None else lens, starts, w.scale, w.num_kv_heads,
+                               w.block_size, w.dtype, w.cache_dtype, w.k_scale, w.v_scale)
+
+
+def pin_prefill_sdpa_causal(O, cache_dtype="f32", q_dtype="f32"):
+    """P13: chunked prefill equals torch's scaled_dot_product_attention (float64) with an explicit
+    bottom-right causal mask, on contiguous K/V rebuilt from an identity block table."""
+    rng = np.random.default_rng(21)
+    H, Hkv, D, B = 8, 2, 16, 16
+    lens, qlens = [5, 23, 70], [5, 7, 33]
+    G = H // Hkv
+    kscale = 0.125 if cache_dtype == "fp8_e4m3" else 1.0
+    vscale = 0.0625 if cache_dtype == "fp8_e4m3" else 1.0
+    nb = [-(-n // B) for n in lens]
+    N = sum(nb)
+    kc = to_store(rng.standard_normal((N, Hkv, B, D)), cache_dtype, kscale)
+    vc = to_store(rng.standard_normal((N, Hkv, B, D)), cache_dtype, vscale)
+    starts = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    q = to_store(rng.standard_normal((int(starts[-1]), H, D)), q_dtype)
+    tables = np.full((3, max(nb)), -1, np.int32)
+    first = np.concatenate([[0], np.cumsum(nb)])
+    for s in range(3):
+        tables[s, :nb[s]] = np.arange(first[s], first[s] + nb[s])
+    scale = float(np.float32(1 / math.sqrt(D)))
+    out = O.prefill_attention(q, kc, vc, tables, np.array(lens, np.int32), starts, scale, Hkv, B, q_dtype,
+                              cache_dtype, kscale, vscale)
+    kv_k, kv_v = torch_value(kc, cache_dtype, kscale), torch_value(vc, cache_dtype, vscale)
+    qv = torch.from_numpy(torch_value(q, q_dtype))
+    for s in range(3):
+        blocks = slice(first[s], first[s] + nb[s])
+        K = torch.from_numpy(kv_k[blocks]).permute(1, 0, 2, 3).reshape(Hkv, -1, D)[:, :lens[s]].repeat_interleave(G, 0)
+        V = torch.from_numpy(kv_v[blocks]).permute(1, 0, 2, 3).reshape(Hkv, -1, D)[:, :lens[s]].repeat_interleave(G, 0)
+        Q = qv[starts[s]:starts[s + 1]].permute(1, 0, 2)                      # [H, qlen, D]
+        i = torch.arange(qlens[s])[:, None]
+        t = torch.arange(lens[s])[None, :]
+        mask = t <= lens[s] - qlens[s] + i                                    # query i sees tokens up to its position
+        ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V, attn_mask=mask, scale=scale)
+        np.testing.assert_allclose(out[starts[s]:starts[s + 1]], ref.permute(1, 0, 2).numpy(), rtol=0, atol=1e-12)
+
+
+def pin_prefill_one_token_is_decode(O, cache_dtype="f32", dtype="f32"):
+    """P14: a chunk of one query (the newest token) is a decode step."""
+    w, q, starts = prefill_case(31, (1, 5, 16, 17, 40), (1, 1, 1, 1, 1), dtype=dtype, cache=cache_dtype)
+    kc, vc = filled(O, w)
+    dec = run_decode(O, w, kc, vc, q=q)
+    pre = run_prefill(O, w, kc, vc, q, starts)
+    np.testing.assert_allclose(pre, dec, rtol=1e-14, atol=1e-15)
+
+
+def pin_prefill_chunks_compose(O):
+    """P15: running a prompt as one chunk or as consecutive chunks (each seeing the tokens before it)
+    gives the same rows; and block permutation leaves the output bitwise unchanged."""
+    w, q, starts = prefill_case(33, (40, 29), (40, 29))
+    kc, vc = filled(O, w)
+    full = run_prefill(O, w, kc, vc, q, starts)
+    for cut in ((0, 17, 40), (0, 1, 16, 33, 40)):
+        rows = []
+        for a, b in zip(cut[:-1], cut[1:]):
+            lens = np.array([b, 0], np.int32)
+            st = np.array([0, b - a, b - a], np.int32)
+            rows.append(run_prefill(O, w, kc, vc, q[a:b], st, lens=lens))
+        assert np.allclose(np.concatenate(rows), full[:40], rtol=0, atol=1e-15)
+    perm = np.random.default_rng(2).permutation(w.num_blocks)
+    kc2, vc2 = np.empty_like(kc), np.empty_like(vc)
+    kc2[perm], vc2[perm] = kc, vc
+    t = w.block_tables.numpy()
+    t2 = np.where(t >= 0, perm[np.maximum(t, 0)], -1).astype(np.int32)
+    assert np.array_equal(run_prefill(O, w, kc2, vc2, q, starts, tables=t2), full)
+
+
 def pin_e4m3_golden(O):
     """P11a: the code table holds the code points printed in the OCP OFP8 specification."""
     vals = O.e4m3_code_values()
@@ -413,6 +494,20 @@ def test_p12_copy_blocks(dtype, cache):
     pin_copy_blocks(oracle, dtype, cache)
 
 
+@pytest.mark.parametrize("cache,qd", [("f32", "f32"), ("bf16", "bf16"), ("fp8_e4m3", "bf16")])
+def test_p13_prefill_sdpa_causal(cache, qd):
+    pin_prefill_sdpa_causal(oracle, cache, qd)
+
+
+@pytest.mark.parametrize("dtype,cache", [("f32", None), ("f16", "fp8_e4m3")])
+def test_p14_prefill_one_token_is_decode(dtype, cache):
+    pin_prefill_one_token_is_decode(oracle, cache, dtype)
+
+
+def test_p15_prefill_chunks_compose():
+    pin_prefill_chunks_compose(oracle)
+
+
 def test_p11_e4m3():
     pin_e4m3_golden(oracle)
     pin_e4m3_nearest_even(oracle)
@@ -445,6 +540,12 @@ MUTANTS = {
     "e4m3 no saturation": ("mag = np.where(a > E4M3_MAX, E4M3_MAX, mag)", "mag = np.where(a > E4M3_MAX, 0.0, mag)"),
     "copy: V not copied": ("v_cache[dst] = v_cache[src]", "v_cache[dst] = v_cache[dst]"),
     "copy: direction reversed": ("k_cache[dst] = k_cache[src]", "k_cache[src] = k_cache[dst]"),
+    "prefill: causal limit one short": ("logits = scale64 * (keys[:p + 1, kv, :] @ qs[h])",
+                                        "logits = scale64 * (keys[:p, kv, :] @ qs[h])"),
+    "prefill: no causal mask": ("p = n - qlen + i                                             # this query's position",
+                                "p = n - 1"),
+    "prefill: position from the chunk start": ("p = n - qlen + i                                             # this query's position",
+                                               "p = i"),
 }
 
 
@@ -465,7 +566,7 @@ def _mutant(find: str, repl: str) -> types.SimpleNamespace:
     exec(compile(src_p, "mut_pa", "exec"), p.__dict__)
     return types.SimpleNamespace(
         decode_attention=p.decode_attention, reshape_and_cache=p.reshape_and_cache, widen=p.widen,
-        copy_blocks=p.copy_blocks,
+        copy_blocks=p.copy_blocks, prefill_attention=p.prefill_attention,
         e4m3_code_values=e.e4m3_code_values, e4m3_encode=e.e4m3_encode, e4m3_decode=e.e4m3_decode)
 
 
@@ -477,6 +578,8 @@ def _runs_clean(O) -> bool:
         lambda: pin_gqa_equals_repeated_mha(O), lambda: pin_reshape_round_trip(O),
         lambda: pin_reshape_locality(O), lambda: pin_e4m3_golden(O), lambda: pin_e4m3_vs_torch(O),
         lambda: pin_fp8_cache_quantisation(O), lambda: pin_copy_blocks(O),
+        lambda: pin_prefill_sdpa_causal(O), lambda: pin_prefill_one_token_is_decode(O),
+        lambda: pin_prefill_chunks_compose(O),
     ]
     for v in variants:
         try:
