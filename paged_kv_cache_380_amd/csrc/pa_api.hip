@@ -166,7 +166,7 @@ int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cach
   if (fp8 && !(std::isfinite(k_scale) && std::isfinite(v_scale) && k_scale > 0.f && v_scale > 0.f))
     return fail(PA_ERR_SHAPE, "prefill: FP8 scales must be finite and positive");
   const int64_t group = num_heads / num_kv_heads;
-  const int64_t row_tiles = ((int64_t)max_query_len * group + 63) / 64;
+  const int64_t row_tiles = ((int64_t)max_query_len * group + pa::kPrefillRows - 1) / pa::kPrefillRows;
   if (row_tiles * num_kv_heads > 0x7fffffffLL)
     return fail(PA_ERR_UNSUPPORTED, "prefill: max_query_len %d too large", max_query_len);
   if (num_seqs == 0 || max_query_len == 0) return ok();

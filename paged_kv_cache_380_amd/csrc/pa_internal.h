@@ -79,10 +79,13 @@ struct PrefillArgs {
   int group;
   int max_blocks;
   int64_t num_blocks;
-  int row_tiles;          // workgroups per KV head and sequence: ceil(max_query_len * group / 64)
+  int row_tiles;          // workgroups per KV head and sequence: ceil(max_query_len * group / kPrefillRows)
   int max_query_len;      // rows of longer chunks past this many tokens are not computed
   int out_kind;
 };
+
+// Rows ((token, head) pairs of one KV head) per prefill workgroup.
+constexpr int kPrefillRows = 64;
 
 hipError_t launch_prefill(const PrefillArgs& a, int q_kind, int cache_kind, hipStream_t stream);
 

@@ -10,8 +10,10 @@
 // How: this is the dense, compute-bound side of paged attention, so it runs
 // as MFMA tiles, flash-attention style (online softmax over key blocks):
 //  * the (token, head) pairs of one KV head form the rows of the problem;
-//    a workgroup of 4 waves takes 64 consecutive rows (row = token * G + head
-//    within the group, so grouped heads share every K/V tile), 16 per wave;
+//    a workgroup of 4 waves takes kPrefillRows consecutive rows (row =
+//    token * G + head within the group, so grouped heads share every K/V
+//    tile), split into 16-row tiles over the waves (one tile per wave was
+//    measured faster than two: the cost per block is not the LDS reads);
 //  * the workgroup streams the sequence's 16-token blocks up to the last
 //    position among its rows. Each block's K and V tile is loaded once, by all
 //    four waves together, into double-buffered LDS (rows padded by 16 bytes
@@ -31,8 +33,9 @@
 namespace pa {
 namespace {
 
-constexpr int kRows = 64;  // rows (token, head pairs) per workgroup, 16 per wave
+constexpr int kRT = kPrefillRows / (16 * kWaves);  // 16-row tiles per wave
 constexpr float kPSlack = 8.0f;
+static_assert(kRT * 16 * kWaves == kPrefillRows, "rows split evenly over the waves");
 
 template <int CK, int D> struct PGeo {
   static constexpr int kBytes = KindBytes<CK>::value;
@@ -67,34 +70,36 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma(const PrefillArgs a) {
   const int ctx = min(a.context_lens[seq], a.max_blocks * 16);
   const int qlen = min(a.query_start_loc[seq + 1] - q0, ctx);  // the chunk: positions ctx - qlen .. ctx - 1
   const int rows = min(qlen, a.max_query_len) * a.group;        // rows computed (the grid covers max_query_len)
-  const int row0 = rt * kRows;
+  const int row0 = rt * kPrefillRows;
   if (row0 >= rows) return;
-  const int last_row = min(row0 + kRows, rows) - 1;
+  const int last_row = min(row0 + kPrefillRows, rows) - 1;
   const int nblk = (ctx - qlen + last_row / a.group + 1 + 15) >> 4;  // blocks up to the last row's position
 
-  // This lane's S column: row n of the wave's 16.
-  const int my_row = row0 + wave * 16 + n;
-  const bool row_ok = my_row < rows;
-  const int my_tok = row_ok ? my_row / a.group : 0;
-  const int my_head = kvh * a.group + (row_ok ? my_row - my_tok * a.group : 0);
-  const int my_limit = row_ok ? ctx - qlen + my_tok + 1 : 0;  // keys visible to this row
-  // The wave's largest limit (its last valid row): blocks at or past it are skipped.
-  const int wave_last = min(row0 + wave * 16 + 15, rows - 1);
-  const int wave_limit = row0 + wave * 16 < rows ? ctx - qlen + wave_last / a.group + 1 : 0;
-
-  uint32_t qf[NKB][4];
-  {
-    const char* qp = static_cast<const char*>(a.q) + ((int64_t)(q0 + my_tok) * a.num_heads + my_head) * D * 2;
+  // This lane's S columns: row n of each of the wave's 16-row tiles.
+  const int wrow0 = row0 + wave * 16 * kRT;
+  int my_limit[kRT];  // keys visible to the row (0 for rows past the chunk)
+  uint32_t qf[kRT][NKB][4];
+#pragma unroll
+  for (int t = 0; t < kRT; ++t) {
+    const int r = wrow0 + t * 16 + n;
+    const bool ok = r < rows;
+    const int tok = ok ? r / a.group : 0;
+    const int head = kvh * a.group + (ok ? r - tok * a.group : 0);
+    my_limit[t] = ok ? ctx - qlen + tok + 1 : 0;
+    const char* qp = static_cast<const char*>(a.q) + ((int64_t)(q0 + tok) * a.num_heads + head) * D * 2;
 #pragma unroll
     for (int b = 0; b < NKB; ++b) {
       uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (row_ok) v = *reinterpret_cast<const uint4*>(qp + (32 * b + 8 * g) * 2);
-      qf[b][0] = v.x;
-      qf[b][1] = v.y;
-      qf[b][2] = v.z;
-      qf[b][3] = v.w;
+      if (ok) v = *reinterpret_cast<const uint4*>(qp + (32 * b + 8 * g) * 2);
+      qf[t][b][0] = v.x;
+      qf[t][b][1] = v.y;
+      qf[t][b][2] = v.z;
+      qf[t][b][3] = v.w;
     }
   }
+  // The wave's largest limit (its last valid row): blocks at or past it are skipped.
+  const int wave_last = min(wrow0 + 16 * kRT - 1, rows - 1);
+  const int wave_limit = wrow0 < rows ? ctx - qlen + wave_last / a.group + 1 : 0;
 
   const int32_t* bt = a.block_tables + (int64_t)seq * a.max_blocks;
   const int64_t blk_stride = (int64_t)a.num_kv_heads * G::kTileBytes;
@@ -146,63 +151,79 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma(const PrefillArgs a) {
     }
   };
 
-  f32x4_t acc[NDB];
+  f32x4_t acc[kRT][NDB];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) acc[db] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-  float mref = kNegInf;
-  float lsum = 0.f;
+  for (int t = 0; t < kRT; ++t)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) acc[t][db] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  float mref[kRT], lsum[kRT];
+#pragma unroll
+  for (int t = 0; t < kRT; ++t) {
+    mref[t] = kNegInf;
+    lsum[t] = 0.f;
+  }
   const float qk_scale = a.qk_scale;
 
   auto compute = [&](int j, int buf) {
     if (j * 16 >= wave_limit) return;  // every row of this wave ends before this block
     const uint16_t* sk = s_k[buf];
     const uint16_t* sv = s_v[buf];
-    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+    f32x4_t s[kRT];
+#pragma unroll
+    for (int t = 0; t < kRT; ++t) s[t] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int b = 0; b < NKB; ++b) {
       const uint4 kw = *reinterpret_cast<const uint4*>(sk + n * S + 32 * b + 8 * g);
       const uint32_t w[4] = {kw.x, kw.y, kw.z, kw.w};
-      s = mma_k32<QK>(w, qf[b], s);
-    }
-    float x[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[i] = s[i] * qk_scale;
-      if (j * 16 + 4 * g + i >= my_limit) x[i] = kNegInf;  // causal limit (and rows past the context)
+      for (int t = 0; t < kRT; ++t) s[t] = mma_k32<QK>(w, qf[t][b], s[t]);
     }
-    const float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    if (__builtin_amdgcn_ballot_w64(bm > mref + kPSlack) != 0) {
-      float bmx = fmaxf(bm, __shfl_xor(bm, 16, 64));
-      bmx = fmaxf(bmx, __shfl_xor(bmx, 32, 64));
-      const float mn = fmaxf(mref, bmx);
-      const float alpha = fast_exp2(mref - ((mn == kNegInf) ? 0.f : mn));
-      lsum *= alpha;
-      mref = mn;
+    uint32_t ph[kRT][2], pl[kRT][2];
+#pragma unroll
+    for (int t = 0; t < kRT; ++t) {
+      float x[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float al = __shfl(alpha, 4 * g + i, 64);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) acc[db][i] *= al;
+        x[i] = s[t][i] * qk_scale;
+        if (j * 16 + 4 * g + i >= my_limit[t]) x[i] = kNegInf;  // causal limit (and rows past the chunk)
       }
-    }
-    const float ms = (mref == kNegInf) ? 0.f : mref;
-    float p[4];
+      const float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      if (__builtin_amdgcn_ballot_w64(bm > mref[t] + kPSlack) != 0) {
+        float bmx = fmaxf(bm, __shfl_xor(bm, 16, 64));
+        bmx = fmaxf(bmx, __shfl_xor(bmx, 32, 64));
+        const float mn = fmaxf(mref[t], bmx);
+        const float alpha = fast_exp2(mref[t] - ((mn == kNegInf) ? 0.f : mn));
+        lsum[t] *= alpha;
+        mref[t] = mn;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[i] = fast_exp2(x[i] - ms);
-      lsum += p[i];
+        for (int i = 0; i < 4; ++i) {
+          const float al = __shfl(alpha, 4 * g + i, 64);
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) acc[t][db][i] *= al;
+        }
+      }
+      const float ms = (mref[t] == kNegInf) ? 0.f : mref[t];
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[i] = fast_exp2(x[i] - ms);
+        lsum[t] += p[i];
+      }
+      ph[t][0] = pack2<QK>(p[0], p[1]);
+      ph[t][1] = pack2<QK>(p[2], p[3]);
+      pl[t][0] = pack2<QK>(p[0] - lo16_to_f32<QK>(ph[t][0]), p[1] - hi16_to_f32<QK>(ph[t][0]));
+      pl[t][1] = pack2<QK>(p[2] - lo16_to_f32<QK>(ph[t][1]), p[3] - hi16_to_f32<QK>(ph[t][1]));
     }
-    const uint32_t h01 = pack2<QK>(p[0], p[1]);
-    const uint32_t h23 = pack2<QK>(p[2], p[3]);
-    const uint32_t l01 = pack2<QK>(p[0] - lo16_to_f32<QK>(h01), p[1] - hi16_to_f32<QK>(h01));
-    const uint32_t l23 = pack2<QK>(p[2] - lo16_to_f32<QK>(h23), p[3] - hi16_to_f32<QK>(h23));
     const uint16_t* vrow = sv + 4 * g * S + n;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       const uint32_t b0 = (uint32_t)vrow[db * 16] | ((uint32_t)vrow[S + db * 16] << 16);
       const uint32_t b1 = (uint32_t)vrow[2 * S + db * 16] | ((uint32_t)vrow[3 * S + db * 16] << 16);
-      acc[db] = mma_k16<QK>(h01, h23, b0, b1, acc[db]);
-      acc[db] = mma_k16<QK>(l01, l23, b0, b1, acc[db]);
+#pragma unroll
+      for (int t = 0; t < kRT; ++t) {
+        acc[t][db] = mma_k16<QK>(ph[t][0], ph[t][1], b0, b1, acc[t][db]);
+        acc[t][db] = mma_k16<QK>(pl[t][0], pl[t][1], b0, b1, acc[t][db]);
+      }
     }
   };
 
@@ -219,25 +240,30 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma(const PrefillArgs a) {
     __syncthreads();
   }
 
-  // Normalise and write this wave's rows: lane (n, g) holds rows 4g + i, column 16 db + n.
-  lsum += __shfl_xor(lsum, 16, 64);
-  lsum += __shfl_xor(lsum, 32, 64);
+  // Normalise and write this wave's rows: lane (n, g) holds rows 4g + i of
+  // each tile, column 16 db + n.
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = row0 + wave * 16 + 4 * g + i;
-    const float L = __shfl(lsum, 4 * g + i, 64);
-    if (r < rows) {
-      const int tok = r / a.group;
-      const int head = kvh * a.group + (r - tok * a.group);
-      const int64_t base = ((int64_t)(q0 + tok) * a.num_heads + head) * D;
-      const float inv = L > 0.f ? a.out_scale / L : 0.f;
+  for (int t = 0; t < kRT; ++t) {
+    float ls = lsum[t];
+    ls += __shfl_xor(ls, 16, 64);
+    ls += __shfl_xor(ls, 32, 64);
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const int64_t e = base + db * 16 + n;
-        const float v = acc[db][i] * inv;
-        if (a.out_kind == kF32) static_cast<float*>(a.out)[e] = v;
-        else if (a.out_kind == kBF16) static_cast<uint16_t*>(a.out)[e] = f32_to_bf16_rne(v);
-        else static_cast<uint16_t*>(a.out)[e] = f32_to_f16_rne(v);
+    for (int i = 0; i < 4; ++i) {
+      const int r = wrow0 + t * 16 + 4 * g + i;
+      const float L = __shfl(ls, 4 * g + i, 64);
+      if (r < rows) {
+        const int tok = r / a.group;
+        const int head = kvh * a.group + (r - tok * a.group);
+        const int64_t base = ((int64_t)(q0 + tok) * a.num_heads + head) * D;
+        const float inv = L > 0.f ? a.out_scale / L : 0.f;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const int64_t e = base + db * 16 + n;
+          const float v = acc[t][db][i] * inv;
+          if (a.out_kind == kF32) static_cast<float*>(a.out)[e] = v;
+          else if (a.out_kind == kBF16) static_cast<uint16_t*>(a.out)[e] = f32_to_bf16_rne(v);
+          else static_cast<uint16_t*>(a.out)[e] = f32_to_f16_rne(v);
+        }
       }
     }
   }
