@@ -26,8 +26,12 @@ bool activation_kind(int k) { return k == PA_DTYPE_F32 || k == PA_DTYPE_F16 || k
 constexpr int64_t kTargetWorkgroups = 512;
 
 int choose_partition_blocks(int num_seqs, int num_heads, int num_kv_heads, int max_blocks) {
+  // Head tiles per KV head as the default kernel for 16-bit queries launches
+  // them (the sizing functions see no dtype; any tile count works, this one
+  // only steers how far contexts are split).
   const int group = num_heads / num_kv_heads;
-  const int64_t tiles = (int64_t)num_seqs * num_kv_heads * (group / pa::group_tile_for(group));
+  const int tile = pa::mfma_group_tile(group) ? pa::mfma_group_tile(group) : pa::group_tile_for(group);
+  const int64_t tiles = (int64_t)num_seqs * num_kv_heads * (group / tile);
   int64_t parts = 1;
   if (tiles > 0 && tiles < kTargetWorkgroups) parts = (kTargetWorkgroups + tiles - 1) / tiles;
   int64_t pb = (max_blocks + parts - 1) / parts;

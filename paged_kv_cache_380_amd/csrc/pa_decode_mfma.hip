@@ -235,13 +235,11 @@ __global__ __launch_bounds__(kThreads) void decode_mfma(const DecodeArgs a) {
     const uint32_t l23 = pack2<QK>(p[2] - lo16_to_f32<QK>(h23), p[3] - hi16_to_f32<QK>(h23));
 
     wave_lds_fence();  // the staged V tile is written
-    const uint16_t* vrow = sv + 4 * g * VS + n;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const uint32_t b0 = (uint32_t)vrow[db * 16] | ((uint32_t)vrow[VS + db * 16] << 16);
-      const uint32_t b1 = (uint32_t)vrow[2 * VS + db * 16] | ((uint32_t)vrow[3 * VS + db * 16] << 16);
-      acc[db] = mma_k16<QK>(h01, h23, b0, b1, acc[db]);
-      acc[db] = mma_k16<QK>(l01, l23, b0, b1, acc[db]);
+      const u32x2_t b = v_operand_tr(sv, VS, db * 16, lane);
+      acc[db] = mma_k16<QK>(h01, h23, b[0], b[1], acc[db]);
+      acc[db] = mma_k16<QK>(l01, l23, b[0], b[1], acc[db]);
     }
   };
 

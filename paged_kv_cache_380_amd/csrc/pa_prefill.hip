@@ -214,15 +214,13 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma(const PrefillArgs a) {
       pl[t][0] = pack2<QK>(p[0] - lo16_to_f32<QK>(ph[t][0]), p[1] - hi16_to_f32<QK>(ph[t][0]));
       pl[t][1] = pack2<QK>(p[2] - lo16_to_f32<QK>(ph[t][1]), p[3] - hi16_to_f32<QK>(ph[t][1]));
     }
-    const uint16_t* vrow = sv + 4 * g * S + n;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const uint32_t b0 = (uint32_t)vrow[db * 16] | ((uint32_t)vrow[S + db * 16] << 16);
-      const uint32_t b1 = (uint32_t)vrow[2 * S + db * 16] | ((uint32_t)vrow[3 * S + db * 16] << 16);
+      const u32x2_t b = v_operand_tr(sv, S, db * 16, lane);
 #pragma unroll
       for (int t = 0; t < kRT; ++t) {
-        acc[t][db] = mma_k16<QK>(ph[t][0], ph[t][1], b0, b1, acc[t][db]);
-        acc[t][db] = mma_k16<QK>(pl[t][0], pl[t][1], b0, b1, acc[t][db]);
+        acc[t][db] = mma_k16<QK>(ph[t][0], ph[t][1], b[0], b[1], acc[t][db]);
+        acc[t][db] = mma_k16<QK>(pl[t][0], pl[t][1], b[0], b[1], acc[t][db]);
       }
     }
   };
