@@ -27,11 +27,20 @@
 //    in place, per lane, with no shuffle of P.
 //  * V must be read token-major per lane, so each wave stages its V tile in
 //    LDS (rows padded by 16 bytes against bank conflicts; FP8 widened to the
-//    16-bit type on the way) and reads the B operand with 2-byte loads.
+//    16-bit type on the way) and reads the B operand back transposed, one
+//    ds_read_b64_tr_b16 per 16 columns.
 //  * P is rounded to the 16-bit type as hi + lo (two MFMAs per D-slice), so the
 //    weights keep about 16 significant bits and the output stays within float32
 //    accumulation error of the exact weights; V, K and q are exact in the
 //    16-bit type (FP8 codes widen exactly).
+//  * When a KV head has several head tiles (more than 16 query heads per KV
+//    head), their workgroups read the same K/V. Then K/V are loaded with the
+//    ordinary (cached) hint and the workgroups are renumbered so that the
+//    tiles of one (sequence, KV head, partition) get consecutive numbers on the
+//    same XCD: the hardware hands workgroups to the 8 XCDs in turn, so dispatch
+//    index i runs on XCD i mod 8, and the tiles that share data then run side
+//    by side behind one L2. With a single tile per KV head nothing is reused
+//    and the loads stay streaming (nontemporal), in launch order.
 //  * The running max is moved lazily: only when a tile's max exceeds it by more
 //    than kSlack (log2 units) is it raised and the accumulators rescaled; all
 //    weights stay below 2^kSlack, which float32 sums hold easily.
@@ -61,12 +70,38 @@ template <int CK, int D> struct MGeo {
   static_assert(NVL >= 1, "tile smaller than one wave-load");
 };
 
+// Workgroup coordinates (x = KV head and head tile, y = partition, z =
+// sequence). With kShared the linear dispatch index is renumbered so that each
+// XCD gets one contiguous range of workgroups: XCD c receives dispatch
+// indices c, c + 8, c + 16, ..., which become numbers start(c), start(c) + 1,
+// ..., with start(c) = c * (total / 8) + min(c, total % 8); this is a
+// bijection onto [0, total).
+template <bool kShared> __device__ __forceinline__ void wg_coords(int& x, int& y, int& z) {
+  if (!kShared) {
+    x = blockIdx.x;
+    y = blockIdx.y;
+    z = blockIdx.z;
+    return;
+  }
+  const unsigned nx = gridDim.x, ny = gridDim.y, total = nx * ny * gridDim.z;
+  const unsigned lin = blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z);
+  const unsigned xcd = lin % 8;
+  const unsigned m = xcd * (total / 8) + min(xcd, total % 8) + lin / 8;
+  x = (int)(m % nx);
+  y = (int)(m / nx % ny);
+  z = (int)(m / (nx * ny));
+}
+
+template <bool kShared> __device__ __forceinline__ uint4 load_kv(const char* p) {
+  return kShared ? *reinterpret_cast<const uint4*>(p) : load_stream(p);
+}
+
 // First element (along D) of the 8 q/K elements lane group g supplies to k block b.
 template <int CK> __device__ __forceinline__ constexpr int k_col(int b, int g) {
   return CK == kFP8 ? 64 * (b >> 1) + 16 * g + 8 * (b & 1) : 32 * b + 8 * g;
 }
 
-template <int QK, int CK, int D, int GT>
+template <int QK, int CK, int D, int GT, bool kShared>
 __global__ __launch_bounds__(kThreads) void decode_mfma(const DecodeArgs a) {
   using G = MGeo<CK, D>;
   constexpr int NKB = G::NKB, NKL = G::NKL, NVL = G::NVL, NDB = G::NDB, VS = G::kVStride;
@@ -79,10 +114,10 @@ __global__ __launch_bounds__(kThreads) void decode_mfma(const DecodeArgs a) {
   __shared__ float s_ml[kWaves * GT * 2];
 
   const int n_sub = a.group / GT;
-  const int kvh = blockIdx.x / n_sub;
-  const int h0 = kvh * a.group + (blockIdx.x - kvh * n_sub) * GT;
-  const int part = blockIdx.y;
-  const int seq = blockIdx.z;
+  int bx, part, seq;
+  wg_coords<kShared>(bx, part, seq);
+  const int kvh = bx / n_sub;
+  const int h0 = kvh * a.group + (bx - kvh * n_sub) * GT;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -144,9 +179,9 @@ __global__ __launch_bounds__(kThreads) void decode_mfma(const DecodeArgs a) {
     const char* kt = kbase + off;
     const char* vt = vbase + off;
 #pragma unroll
-    for (int c = 0; c < NKL; ++c) kr[c] = load_stream(kt + k_off + c * 64);
+    for (int c = 0; c < NKL; ++c) kr[c] = load_kv<kShared>(kt + k_off + c * 64);
 #pragma unroll
-    for (int c = 0; c < NVL; ++c) vr[c] = load_stream(vt + v_off + c * 1024);
+    for (int c = 0; c < NVL; ++c) vr[c] = load_kv<kShared>(vt + v_off + c * 1024);
   };
 
   auto process = [&](auto masked, int j, const Tile& t) {
@@ -278,7 +313,10 @@ __global__ __launch_bounds__(kThreads) void decode_mfma(const DecodeArgs a) {
 template <int QK, int CK, int D, int GT>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)(a.num_kv_heads * (a.group / GT)), (unsigned)a.num_parts, (unsigned)a.num_seqs);
-  decode_mfma<QK, CK, D, GT><<<grid, dim3(kThreads), 0, stream>>>(a);
+  if (a.group > GT)
+    decode_mfma<QK, CK, D, GT, true><<<grid, dim3(kThreads), 0, stream>>>(a);
+  else
+    decode_mfma<QK, CK, D, GT, false><<<grid, dim3(kThreads), 0, stream>>>(a);
   return hipGetLastError();
 }
 
