@@ -327,7 +327,8 @@ def main():
         "config": {
             "workload": w.name, "num_seqs": w.num_seqs, "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads,
             "head_size": w.head_size, "block_size": w.block_size, "context_tokens": int(w.context_lens.sum()),
-            "kv_cache_dtype": w.cache_dtype, "partition_blocks": pb, "seed": w.seed,
+            "kv_cache_dtype": w.cache_dtype, "seed": w.seed,
+            "schedule": "balanced" if balanced_schedule(w, args.partition_blocks) else f"partitions of {pb} blocks",
             "decode_path": os.environ.get("PA_DECODE_PATH", "auto"),
         },
         "pct_of_hbm_peak": round(100 * kv_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
@@ -335,7 +336,7 @@ def main():
         "decode_ms": round(decode_ms, 5),
         "decode_ms_p10_p90": [round(durs[len(durs) // 10], 5), round(durs[(9 * len(durs)) // 10], 5)],
         "roofline": {
-            "kernel": decode_kernel(w) + ("" if wl_parts(w, pb) == 1 else " + decode_reduce"),
+            "kernel": decode_kernels(w, args.partition_blocks, pb),
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": None if traffic is None else round(traffic),
@@ -454,6 +455,18 @@ def decode_kernel(w) -> str:
 
 def wl_parts(w, pb: int) -> int:
     return -(-w.max_blocks_per_seq // pb)
+
+
+def balanced_schedule(w, partition_blocks: int) -> bool:
+    """Whether the library picks its balanced schedule here (its selection rule, restated)."""
+    return (decode_kernel(w) == "decode_mfma" and partition_blocks == 0 and w.num_seqs <= 1024
+            and w.num_seqs * w.max_blocks_per_seq <= 2**31 - 1)
+
+
+def decode_kernels(w, partition_blocks: int, pb: int) -> str:
+    if balanced_schedule(w, partition_blocks):
+        return "decode_mfma[balanced] + decode_bal_reduce"
+    return decode_kernel(w) + ("" if wl_parts(w, pb) == 1 else " + decode_reduce")
 
 
 if __name__ == "__main__":

@@ -131,10 +131,17 @@ int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void
  *                   a call running concurrently.
  *   stream          hipStream_t to queue on
  *
- * A context longer than one partition (chosen on the host from the shapes) is
- * split: each partition writes its running max, sum and unnormalised output
- * to the workspace, and a second kernel merges the partitions in a fixed
- * order, so results are deterministic run to run.
+ * Schedules. Partitioned: a context longer than one partition (its length
+ * chosen on the host from the shapes) is split; each partition writes its
+ * running max, sum and unnormalised output to the workspace, and a second
+ * kernel merges the partitions. Balanced (the library's own choice for the
+ * matrix-core kernel, when num_seqs <= 1024 and the workspace holds
+ * pa_decode_workspace_bytes(..., 0) bytes): the blocks of all sequences, laid
+ * end to end, are cut into equal ranges, one per wave, whatever the context
+ * lengths, so a ragged batch keeps every wave busy to the end; pieces of a
+ * sequence cut by a range boundary are merged by a second kernel. With a
+ * smaller or NULL workspace the partitioned schedule runs (and may itself
+ * need one). Both merge in a fixed order: results are deterministic run to run.
  *
  * Kernel choice: with F16/BF16 queries and a multiple of 4 query heads per
  * KV head, the products of a K/V tile with the group's queries run on the
@@ -187,9 +194,9 @@ int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cach
  * pa_decode_split -- pa_decode with an explicit partition length.
  *
  * partition_blocks = number of 16-token blocks per partition, a multiple of 4
- * in [4, 512], or 0 for the library's own choice (then identical to pa_decode).
- * Results equal pa_decode's up to float32 rounding order. Used to exercise and
- * time given split factors.
+ * in [4, 512] (the partitioned schedule), or 0 for the library's own choice
+ * (then identical to pa_decode). Results equal pa_decode's up to float32
+ * rounding order. Used to exercise and time given split factors.
  */
 int pa_decode_split(void* out, const void* q, const void* k_cache, const void* v_cache,
                     const int32_t* block_tables, const int32_t* context_lens, float scale,
@@ -200,9 +207,15 @@ int pa_decode_split(void* out, const void* q, const void* k_cache, const void* v
 
 /*
  * pa_decode_workspace_bytes -- workspace size pa_decode / pa_decode_split need
- * for these shapes (0 when no sequence can span two partitions). Pure
- * function of its arguments; returns 0 for invalid shapes.
- * partition_blocks as in pa_decode_split (0 = the library's choice).
+ * for these shapes. Pure function of its arguments; returns 0 for invalid
+ * shapes. partition_blocks as in pa_decode_split. With a partition length:
+ * the partitioned schedule's need (0 when no sequence can span two
+ * partitions). With 0 (the library's choice), which sees no dtype: the larger
+ * of the partitioned need and, where the balanced schedule can apply (a
+ * multiple of 4 query heads per KV head, num_seqs <= 1024), its need of
+ * num_heads * (num_seqs + R) * (head_size + 2) floats plus num_seqs + 1 ints,
+ * R being its number of ranges (for this size, the larger count it takes
+ * with an FP8 cache; a 16-bit cache takes half as many ranges).
  */
 size_t pa_decode_workspace_bytes(int num_seqs, int num_heads, int num_kv_heads, int head_size,
                                  int max_blocks_per_seq, int block_size, int partition_blocks);

@@ -69,10 +69,42 @@ bool shapes_ok(int num_seqs, int num_heads, int num_kv_heads, int head_size, int
 struct Layout {
   int partition_blocks;
   int num_parts;
-  size_t out_bytes;  // partition outputs, at offset 0
-  size_t ml_offset;  // partition max/sum pairs
+  size_t out_bytes;    // partition outputs, at offset 0
+  size_t ml_offset;    // partition max/sum pairs
+  size_t pref_offset;  // balanced schedule: per-sequence block prefix
   size_t total;
 };
+
+// Balanced schedule of the matrix-core kernel: the blocks of all sequences
+// are cut into R equal ranges, one per wave, R a multiple of 4 (a workgroup
+// takes four ranges). R aims at kBalancedWaves16 waves in all for 16-bit
+// caches, one 4-wave workgroup per CU (more, shorter waves measured slower:
+// each pays the start of its stream), and at twice that for FP8 caches, whose
+// tiles carry half the bytes for more vector work (widening), so that a
+// second wave per SIMD hides one wave's arithmetic behind the other's loads.
+constexpr int kBalancedWaves16 = 1024;
+constexpr int kBalancedWavesFp8 = 2048;
+
+bool balanced_fits(int num_seqs, int max_blocks) {
+  return num_seqs <= pa::kBalancedMaxSeqs && (int64_t)num_seqs * max_blocks <= 0x7fffffffLL;
+}
+
+int64_t balanced_ranges(int num_heads, int group_tile, bool fp8_cache) {
+  const int64_t columns = num_heads / group_tile;
+  const int64_t waves = fp8_cache ? kBalancedWavesFp8 : kBalancedWaves16;
+  const int64_t r = (waves + columns - 1) / columns;
+  return (r + 3) / 4 * 4;
+}
+
+Layout balanced_layout(int num_seqs, int num_heads, int head_size, int64_t ranges) {
+  Layout L{};
+  const size_t rows = (size_t)num_heads * ((size_t)num_seqs + ranges);
+  L.out_bytes = rows * head_size * sizeof(float);
+  L.ml_offset = (L.out_bytes + 255) / 256 * 256;
+  L.pref_offset = (L.ml_offset + rows * 2 * sizeof(float) + 255) / 256 * 256;
+  L.total = L.pref_offset + ((size_t)num_seqs + 1) * sizeof(int);
+  return L;
+}
 
 Layout workspace_layout(int num_seqs, int num_heads, int head_size, int max_blocks, int pb) {
   Layout L{};
@@ -211,10 +243,20 @@ int pa_decode_partition_blocks(int num_seqs, int num_heads, int num_kv_heads, in
 size_t pa_decode_workspace_bytes(int num_seqs, int num_heads, int num_kv_heads, int head_size,
                                  int max_blocks_per_seq, int block_size, int partition_blocks) {
   if (!shapes_ok(num_seqs, num_heads, num_kv_heads, head_size, max_blocks_per_seq, block_size)) return 0;
-  if (partition_blocks == 0)
+  size_t balanced = 0;
+  if (partition_blocks == 0) {
+    // The kernel family depends on the query dtype and the balanced range
+    // count on the cache dtype, neither of which this function sees: size for
+    // the largest need the choice may have (FP8's range count is the larger).
+    const int tile = pa::mfma_group_tile(num_heads / num_kv_heads);
+    if (tile && balanced_fits(num_seqs, max_blocks_per_seq) && num_seqs > 0)
+      balanced = balanced_layout(num_seqs, num_heads, head_size,
+                                 balanced_ranges(num_heads, tile, /*fp8_cache=*/true)).total;
     partition_blocks = choose_partition_blocks(num_seqs, num_heads, num_kv_heads, max_blocks_per_seq);
+  }
   if (partition_blocks < 4 || partition_blocks > pa::kMaxPartitionBlocks || partition_blocks % 4) return 0;
-  return workspace_layout(num_seqs, num_heads, head_size, max_blocks_per_seq, partition_blocks).total;
+  const size_t split = workspace_layout(num_seqs, num_heads, head_size, max_blocks_per_seq, partition_blocks).total;
+  return split > balanced ? split : balanced;
 }
 
 int pa_decode_split(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -252,9 +294,22 @@ int pa_decode_split(void* out, const void* q, const void* k_cache, const void* v
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
     return fail(PA_ERR_NULL, "decode: NULL pointer argument");
 
+  const int group = num_heads / num_kv_heads;
+  const bool mfma = use_mfma(q_dtype, group);
+  const int group_tile = mfma ? pa::mfma_group_tile(group) : pa::group_tile_for(group);
+  // The library's own choice for the matrix-core kernel is the balanced
+  // schedule; an explicit partition length selects the partitioned one.
+  // It needs a workspace; a caller that passes none (or too small a one, as
+  // sized before this schedule existed) gets the partitioned schedule.
+  bool balanced = partition_blocks == 0 && mfma && balanced_fits(num_seqs, max_blocks_per_seq);
+  const int64_t ranges = balanced ? balanced_ranges(num_heads, group_tile, fp8) : 0;
+  if (balanced && (!workspace || workspace_bytes < balanced_layout(num_seqs, num_heads, head_size, ranges).total))
+    balanced = false;
+  if (ranges / 4 > 65535) return fail(PA_ERR_UNSUPPORTED, "decode: too many ranges (%lld)", (long long)ranges);
   const int pb = partition_blocks ? partition_blocks
                                   : choose_partition_blocks(num_seqs, num_heads, num_kv_heads, max_blocks_per_seq);
-  const Layout L = workspace_layout(num_seqs, num_heads, head_size, max_blocks_per_seq, pb);
+  const Layout L = balanced ? balanced_layout(num_seqs, num_heads, head_size, ranges)
+                            : workspace_layout(num_seqs, num_heads, head_size, max_blocks_per_seq, pb);
   if (L.num_parts > 65535) return fail(PA_ERR_UNSUPPORTED, "decode: too many partitions (%d)", L.num_parts);
   if (L.total > 0) {
     if (!workspace)
@@ -275,6 +330,7 @@ int pa_decode_split(void* out, const void* q, const void* k_cache, const void* v
   a.context_lens = context_lens;
   a.ws_out = L.total ? static_cast<float*>(workspace) : nullptr;
   a.ws_ml = L.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + L.ml_offset) : nullptr;
+  a.ws_pref = balanced ? reinterpret_cast<int*>(static_cast<char*>(workspace) + L.pref_offset) : nullptr;
   const double log2e = 1.4426950408889634;
   a.qk_scale = (float)((double)scale * log2e * (fp8 ? (double)k_scale : 1.0));
   a.out_scale = fp8 ? v_scale : 1.0f;
@@ -282,9 +338,11 @@ int pa_decode_split(void* out, const void* q, const void* k_cache, const void* v
   a.num_heads = num_heads;
   a.num_kv_heads = num_kv_heads;
   a.head_size = head_size;
-  a.group = num_heads / num_kv_heads;
-  a.use_mfma = use_mfma(q_dtype, a.group) ? 1 : 0;
-  a.group_tile = a.use_mfma ? pa::mfma_group_tile(a.group) : pa::group_tile_for(a.group);
+  a.group = group;
+  a.use_mfma = mfma ? 1 : 0;
+  a.group_tile = group_tile;
+  a.balanced = balanced ? 1 : 0;
+  a.ranges = balanced ? (int)ranges : 0;
   a.num_blocks = num_blocks;
   a.max_blocks = max_blocks_per_seq;
   a.partition_blocks = pb;

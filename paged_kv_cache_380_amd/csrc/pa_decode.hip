@@ -643,6 +643,74 @@ __global__ __launch_bounds__(64) void decode_reduce(const DecodeArgs a) {
   for (int k = 0; k < D / 64; ++k) store_out(a, sh * D + lane + 64 * k, O[k] / L);
 }
 
+// Merge the pieces of every (sequence, head) that the balanced schedule of
+// the matrix-core kernel cut: ranges r_lo .. r_hi (those of them that hold
+// any block) each left one piece in slot seq + r. Sequences held by a single
+// range were written by the kernel itself; empty ones get zeros here.
+template <int D>
+__global__ __launch_bounds__(64) void decode_bal_reduce(const DecodeArgs a) {
+  __shared__ float s_f[64];
+  const int h = blockIdx.x;
+  const int seq = blockIdx.y;
+  const int lane = threadIdx.x;
+  const int ps = a.ws_pref[seq];
+  const int pe = a.ws_pref[seq + 1];
+  const int64_t T = a.ws_pref[a.num_seqs];
+  const int64_t sh = (int64_t)seq * a.num_heads + h;
+  if (ps >= pe) {
+#pragma unroll
+    for (int k = 0; k < D / 64; ++k) store_out(a, sh * D + lane + 64 * k, 0.f);
+    return;
+  }
+  // Range r holds positions [floor(r T / R), floor((r + 1) T / R)); r_lo and
+  // r_hi are the last ranges starting at or before the first and the last
+  // block of the sequence.
+  const int64_t R = a.ranges;
+  const int r_lo = (int)(((int64_t)(ps + 1) * R + T - 1) / T) - 1;
+  const int r_hi = (int)(((int64_t)pe * R + T - 1) / T) - 1;
+  if (r_lo >= r_hi) return;
+  const int pieces = r_hi - r_lo + 1;
+  const int64_t slots = (int64_t)a.num_seqs + R;
+  const float* ml = a.ws_ml + ((int64_t)h * slots + seq + r_lo) * 2;
+  const float* o = a.ws_out + ((int64_t)h * slots + seq + r_lo) * D;
+  auto held = [&](int i) { return (int64_t)(r_lo + i) * T / R < (int64_t)(r_lo + i + 1) * T / R; };
+  // Maxima and sums with the lanes across the pieces.
+  float M = kNegInf;
+  for (int i = lane; i < pieces; i += 64)
+    if (held(i)) M = fmaxf(M, ml[2 * i]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+  float L = 0.f;
+  for (int i = lane; i < pieces; i += 64)
+    if (held(i)) L += ml[2 * i + 1] * fast_exp2(ml[2 * i] - M);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off, 64);
+  // Outputs: 64 pieces at a time, their weights staged in LDS (0 for ranges
+  // that hold no block; their slots were never written and are skipped by
+  // selection, not multiplied).
+  float O[D / 64];
+#pragma unroll
+  for (int k = 0; k < D / 64; ++k) O[k] = 0.f;
+  for (int base = 0; base < pieces; base += 64) {
+    const int i = base + lane;
+    wave_lds_fence();
+    s_f[lane] = (i < pieces && held(i)) ? fast_exp2(ml[2 * i] - M) : 0.f;
+    wave_lds_fence();
+    const int n = min(64, pieces - base);
+#pragma unroll 8
+    for (int j = 0; j < n; ++j) {
+      const float f = s_f[j];
+#pragma unroll
+      for (int k = 0; k < D / 64; ++k) {
+        const float v = o[(int64_t)(base + j) * D + lane + 64 * k];
+        O[k] += f != 0.f ? v * f : 0.f;
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < D / 64; ++k) store_out(a, sh * D + lane + 64 * k, O[k] / L);
+}
+
 template <int QK, int CK, int D, int GT>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)(a.num_kv_heads * (a.group / GT)), (unsigned)a.num_parts, (unsigned)a.num_seqs);
@@ -689,7 +757,17 @@ hipError_t launch_decode(const DecodeArgs& a, int q_kind, int cache_kind, hipStr
       default: return hipErrorInvalidValue;
     }
   }
-  if (e != hipSuccess || a.num_parts == 1) return e;
+  if (e != hipSuccess) return e;
+  if (a.balanced) {
+    const dim3 grid((unsigned)a.num_heads, (unsigned)a.num_seqs);
+    switch (a.head_size) {
+      case 64: decode_bal_reduce<64><<<grid, dim3(64), 0, stream>>>(a); break;
+      case 128: decode_bal_reduce<128><<<grid, dim3(64), 0, stream>>>(a); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
+  if (a.num_parts == 1) return e;
   switch (a.head_size) {
     case 64: decode_reduce<64><<<dim3((unsigned)a.num_heads, (unsigned)a.num_seqs), dim3(64), 0, stream>>>(a); break;
     case 128: decode_reduce<128><<<dim3((unsigned)a.num_heads, (unsigned)a.num_seqs), dim3(64), 0, stream>>>(a); break;

@@ -56,6 +56,7 @@ namespace {
 
 constexpr float kSlack = 8.0f;    // lazy-max slack, log2 units
 constexpr int kRing = 2;          // register ring depth: blocks per wave in flight, plus the one in use
+constexpr int kRingBalanced = 2;  // the same for the balanced schedule
 
 // Geometry of one (block, KV head) tile for the MFMA kernel.
 template <int CK, int D> struct MGeo {
@@ -101,7 +102,7 @@ template <int CK> __device__ __forceinline__ constexpr int k_col(int b, int g) {
   return CK == kFP8 ? 64 * (b >> 1) + 16 * g + 8 * (b & 1) : 32 * b + 8 * g;
 }
 
-template <int QK, int CK, int D, int GT, bool kShared>
+template <int QK, int CK, int D, int GT, bool kShared, bool kBalanced>
 __global__ __launch_bounds__(kThreads) void decode_mfma(const DecodeArgs a) {
   using G = MGeo<CK, D>;
   constexpr int NKB = G::NKB, NKL = G::NKL, NVL = G::NVL, NDB = G::NDB, VS = G::kVStride;
@@ -110,11 +111,13 @@ __global__ __launch_bounds__(kThreads) void decode_mfma(const DecodeArgs a) {
 
   __shared__ int s_blocks[kMaxPartitionBlocks];
   __shared__ __align__(16) uint16_t s_v[kWaves][16 * VS];
-  __shared__ float s_acc[kWaves * GT * D];
-  __shared__ float s_ml[kWaves * GT * 2];
+  __shared__ float s_acc[kBalanced ? 1 : kWaves * GT * D];
+  __shared__ float s_ml[kBalanced ? 1 : kWaves * GT * 2];
+  __shared__ int s_pref[kBalanced ? kBalancedMaxSeqs + 1 : 1];
+  __shared__ int s_scan[kBalanced ? kWaves : 1];
 
   const int n_sub = a.group / GT;
-  int bx, part, seq;
+  int bx, part, seq;  // balanced: part is the group of four ranges, seq is set per piece
   wg_coords<kShared>(bx, part, seq);
   const int kvh = bx / n_sub;
   const int h0 = kvh * a.group + (bx - kvh * n_sub) * GT;
@@ -124,25 +127,15 @@ __global__ __launch_bounds__(kThreads) void decode_mfma(const DecodeArgs a) {
   const int n = lane & 15;  // token of K rows / head of S columns and P rows / column of O
   const int g = lane >> 4;  // k group of the operands / row group of the results
 
-  const int ctx = context_len(a, seq);
-  if (ctx <= 0) {
-    write_zeros<GT, D>(a, seq, h0, part, tid);
-    return;
-  }
-  const int seq_blocks = (ctx + 15) >> 4;
-  const int blk0 = part * a.partition_blocks;
-  if (blk0 >= seq_blocks) return;
-  const int nblk = min(a.partition_blocks, seq_blocks - blk0);
-  const int seq_parts = (seq_blocks + a.partition_blocks - 1) / a.partition_blocks;
-
-  const int32_t* bt = a.block_tables + (int64_t)seq * a.max_blocks + blk0;
-  for (int j = tid; j < nblk; j += kThreads) s_blocks[j] = bt[j];
+  int ctx = 0;     // context length of the sequence in hand
+  int blk0 = 0;    // its first block handled here (partition start, or start of the piece)
+  int sb_off = 0;  // entry of s_blocks holding block blk0
 
   // q as the B operand of S = K·Qᵀ: lane (n, g) holds head h0 + n, the 8
   // elements of k block b that group g supplies; heads past the tile are zero.
   uint32_t qf[NKB][4];
-  {
-    const char* qp = static_cast<const char*>(a.q) + ((int64_t)seq * a.num_heads + h0 + n) * D * 2;
+  auto load_q = [&](int s) {
+    const char* qp = static_cast<const char*>(a.q) + ((int64_t)s * a.num_heads + h0 + n) * D * 2;
 #pragma unroll
     for (int b = 0; b < NKB; ++b) {
       uint4 v = make_uint4(0u, 0u, 0u, 0u);
@@ -152,14 +145,17 @@ __global__ __launch_bounds__(kThreads) void decode_mfma(const DecodeArgs a) {
       qf[b][2] = v.z;
       qf[b][3] = v.w;
     }
-  }
-  __syncthreads();
+  };
 
   f32x4_t acc[NDB];
+  float mref;  // running reference max of head n (log2 units), equal on lanes n, n+16, n+32, n+48
+  float lsum;  // this lane's share of the running sum of head n
+  auto reset = [&]() {
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) acc[db] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-  float mref = kNegInf;  // running reference max of head n (log2 units), equal on lanes n, n+16, n+32, n+48
-  float lsum = 0.f;      // this lane's share of the running sum of head n
+    for (int db = 0; db < NDB; ++db) acc[db] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    mref = kNegInf;
+    lsum = 0.f;
+  };
 
   const int64_t blk_stride = (int64_t)a.num_kv_heads * G::kTileBytes;
   const char* kbase = static_cast<const char*>(a.k_cache) + (int64_t)kvh * G::kTileBytes;
@@ -175,7 +171,8 @@ __global__ __launch_bounds__(kThreads) void decode_mfma(const DecodeArgs a) {
   auto load_tile = [&](int j, Tile& t) {
     uint4(&kr)[NKL] = t.k;
     uint4(&vr)[NVL] = t.v;
-    const int64_t off = pool_block(a, s_blocks, j) * blk_stride;
+    const int64_t off = pool_block(a, kBalanced ? s_blocks + wave * (kMaxPartitionBlocks / kWaves) : s_blocks,
+                                   sb_off + j) * blk_stride;
     const char* kt = kbase + off;
     const char* vt = vbase + off;
 #pragma unroll
@@ -278,45 +275,225 @@ __global__ __launch_bounds__(kThreads) void decode_mfma(const DecodeArgs a) {
     }
   };
 
-  // The block holding rows past the context (the last of the sequence, when
-  // its length is not a multiple of 16) runs after the steady stream, by the
-  // wave that owns it, so the stream's loop body holds one unmasked block
-  // per ring slot and the accumulators stay in place across iterations.
-  const bool tail_masked = (ctx & 15) && blk0 + nblk == seq_blocks;
-  const int n_full = nblk - (tail_masked ? 1 : 0);
-  stream_blocks<kRing, Tile>(wave, kWaves, n_full, load_tile,
-                      [&](int j, const Tile& t) { process(std::false_type{}, j, t); });
-  if (tail_masked && n_full % kWaves == wave) {
-    Tile t;
-    load_tile(n_full, t);
-    process(std::true_type{}, n_full, t);
-  }
+  // Blocks blk0 + first, blk0 + first + step, ... below blk0 + nblk of a
+  // sequence holding seq_blocks blocks. The block holding rows past the
+  // context (the last of the sequence, when its length is not a multiple of
+  // 16) runs after the steady stream, by the wave that owns it, so the
+  // stream's loop body holds one unmasked block per ring slot and the
+  // accumulators stay in place across iterations.
+  auto run_blocks = [&](int first, int step, int nblk, int seq_blocks) {
+    const bool tail_masked = (ctx & 15) && blk0 + nblk == seq_blocks;
+    const int n_full = nblk - (tail_masked ? 1 : 0);
+    if constexpr (kBalanced) {
+      // One wave per piece, registers to spare: the masked block's loads go
+      // out first, so they arrive with the stream's first block instead of
+      // after its last.
+      Tile tm;
+      if (tail_masked) load_tile(n_full, tm);
+      stream_blocks<kRingBalanced, Tile>(0, 1, n_full, load_tile,
+                                         [&](int j, const Tile& t) { process(std::false_type{}, j, t); });
+      if (tail_masked) process(std::true_type{}, n_full, tm);
+    } else {
+      stream_blocks<kRing, Tile>(first, step, n_full, load_tile,
+                                 [&](int j, const Tile& t) { process(std::false_type{}, j, t); });
+      if (tail_masked && n_full % step == first) {
+        Tile t;
+        load_tile(n_full, t);
+        process(std::true_type{}, n_full, t);
+      }
+    }
+  };
 
-  // This wave's sum of head n over its four row groups; the max is already shared.
-  lsum += __shfl_xor(lsum, 16, 64);
-  lsum += __shfl_xor(lsum, 32, 64);
-  if (g == 0 && n < GT) {
-    s_ml[(wave * GT + n) * 2] = mref;
-    s_ml[(wave * GT + n) * 2 + 1] = lsum;
-  }
+  if constexpr (!kBalanced) {
+    // One partition of one sequence; the four waves take its blocks in turn.
+    ctx = context_len(a, seq);
+    if (ctx <= 0) {
+      write_zeros<GT, D>(a, seq, h0, part, tid);
+      return;
+    }
+    const int seq_blocks = (ctx + 15) >> 4;
+    blk0 = part * a.partition_blocks;
+    if (blk0 >= seq_blocks) return;
+    const int nblk = min(a.partition_blocks, seq_blocks - blk0);
+    const int seq_parts = (seq_blocks + a.partition_blocks - 1) / a.partition_blocks;
+
+    const int32_t* bt = a.block_tables + (int64_t)seq * a.max_blocks + blk0;
+    for (int j = tid; j < nblk; j += kThreads) s_blocks[j] = bt[j];
+    load_q(seq);
+    __syncthreads();
+
+    reset();
+    run_blocks(wave, kWaves, nblk, seq_blocks);
+
+    // This wave's sum of head n over its four row groups; the max is already shared.
+    lsum += __shfl_xor(lsum, 16, 64);
+    lsum += __shfl_xor(lsum, 32, 64);
+    if (g == 0 && n < GT) {
+      s_ml[(wave * GT + n) * 2] = mref;
+      s_ml[(wave * GT + n) * 2 + 1] = lsum;
+    }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (4 * g + i < GT) {
+    for (int i = 0; i < 4; ++i) {
+      if (4 * g + i < GT) {
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) s_acc[(wave * GT + 4 * g + i) * D + db * 16 + n] = acc[db][i];
+        for (int db = 0; db < NDB; ++db) s_acc[(wave * GT + 4 * g + i) * D + db * 16 + n] = acc[db][i];
+      }
+    }
+    __syncthreads();
+    finish_partition<GT, D>(a, s_acc, s_ml, seq, h0, part, seq_parts, tid);
+  } else {
+    // Balanced schedule. The blocks of all sequences, laid end to end in
+    // sequence order, are T positions; range r of R holds positions
+    // [B(r), B(r + 1)) with B(r) = floor(r * T / R), and wave w of this
+    // workgroup takes range 4 * part + w whole, cutting sequences wherever
+    // the ranges fall. The piece of a sequence that a range holds is
+    // streamed like a partition; a sequence held entirely by one range is
+    // written straight to the output, any other piece leaves its max, sum
+    // and unnormalised output in slot s + r of the workspace for
+    // decode_bal_reduce. Every workgroup first builds the block-count
+    // prefix of the batch in LDS (one pass over context_lens).
+    const int S = a.num_seqs;
+    // Blocks per sequence and their exclusive prefix sum s_pref[0..S].
+    constexpr int kPer = (kBalancedMaxSeqs + kThreads - 1) / kThreads;
+    const int per = (S + kThreads - 1) / kThreads;
+    int nb[kPer];
+    int local = 0;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int s = tid * per + k;
+      int c = 0;
+      if (k < per && s < S) c = context_len(a, s);
+      nb[k] = c > 0 ? (c + 15) >> 4 : 0;
+      local += nb[k];
+    }
+    // Inclusive scan of the per-thread sums: within each wave by shuffles,
+    // then across the four waves through LDS.
+    int incl = local;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += t;
+    }
+    if (lane == 63) s_scan[wave] = incl;
+    __syncthreads();
+    {
+      int run = incl - local;
+      for (int w = 0; w < wave; ++w) run += s_scan[w];
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) {
+        const int s = tid * per + k;
+        if (k < per && s < S) s_pref[s] = run;
+        run += nb[k];
+      }
+      if (tid == kThreads - 1) s_pref[S] = run;
+    }
+    __syncthreads();
+    const int T = s_pref[S];
+    const int64_t R = a.ranges;
+    auto range_start = [&](int64_t r) { return (int)(r * T / R); };
+    // Sequence holding position p < T: the last s with s_pref[s] <= p (empty
+    // sequences share their successor's start and are passed over).
+    auto seq_of = [&](int p) {
+      int lo = 0, hi = S;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_pref[mid] <= p) lo = mid;
+        else hi = mid;
+      }
+      return lo;
+    };
+    if (blockIdx.x == 0 && blockIdx.y == 0)
+      for (int k = tid; k <= S; k += kThreads) a.ws_pref[k] = s_pref[k];
+
+    // Each wave stages the block ids of its range in LDS, a window of
+    // kWindow positions at a time (no workgroup barrier: the window is the
+    // wave's own quarter of s_blocks).
+    constexpr int kWindow = kMaxPartitionBlocks / kWaves;
+    int* const wblocks = s_blocks + wave * kWindow;
+    int win = 0, win_end = 0;
+    auto stage = [&](int from, int to) {
+      wave_lds_fence();  // the previous window's reads are issued
+      for (int i = lane; i < to - from; i += 64) {
+        const int p = from + i;
+        const int s = seq_of(p);
+        wblocks[i] = a.block_tables[(int64_t)s * a.max_blocks + (p - s_pref[s])];
+      }
+      wave_lds_fence();
+      win = from;
+      win_end = to;
+    };
+
+    const int r = 4 * part + wave;
+    const int r_end = range_start(r + 1);
+    const int64_t slots = (int64_t)S + R;
+    for (int pos = range_start(r); pos < r_end;) {
+      seq = __builtin_amdgcn_readfirstlane(seq_of(pos));
+      const int ps = s_pref[seq], pe = s_pref[seq + 1];
+      const int piece_end = min(r_end, pe);
+      ctx = context_len(a, seq);
+      load_q(seq);
+      reset();
+      // The piece [pos, piece_end), window by window, accumulating throughout.
+      for (int sub = pos; sub < piece_end;) {
+        if (sub >= win_end) stage(sub, min(sub + kWindow, r_end));
+        const int sub_end = min(piece_end, win_end);
+        blk0 = sub - ps;
+        sb_off = sub - win;
+        run_blocks(0, 1, sub_end - sub, pe - ps);
+        sub = sub_end;
+      }
+
+      float ls = lsum + __shfl_xor(lsum, 16, 64);
+      ls += __shfl_xor(ls, 32, 64);
+      if (pos == ps && piece_end == pe) {
+        // The whole sequence: normalise and write the output rows 4g + i.
+        float inv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) inv[i] = a.out_scale / __shfl(ls, 4 * g + i, 64);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (4 * g + i < GT) {
+            const int64_t row = ((int64_t)seq * a.num_heads + h0 + 4 * g + i) * D;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) store_out(a, row + db * 16 + n, acc[db][i] * inv[i]);
+          }
+        }
+      } else {
+        const int64_t slot = seq + r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (4 * g + i < GT) {
+            float* o = a.ws_out + ((int64_t)(h0 + 4 * g + i) * slots + slot) * D;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) o[db * 16 + n] = acc[db][i] * a.out_scale;
+          }
+        }
+        if (g == 0 && n < GT) {
+          float* ml = a.ws_ml + ((int64_t)(h0 + n) * slots + slot) * 2;
+          ml[0] = mref;
+          ml[1] = ls;
+        }
+      }
+      pos = piece_end;
     }
   }
-  __syncthreads();
-  finish_partition<GT, D>(a, s_acc, s_ml, seq, h0, part, seq_parts, tid);
+}
+
+template <int QK, int CK, int D, int GT, bool kBalanced>
+void launch_s(const DecodeArgs& a, dim3 grid, hipStream_t stream) {
+  if (a.group > GT)
+    decode_mfma<QK, CK, D, GT, true, kBalanced><<<grid, dim3(kThreads), 0, stream>>>(a);
+  else
+    decode_mfma<QK, CK, D, GT, false, kBalanced><<<grid, dim3(kThreads), 0, stream>>>(a);
 }
 
 template <int QK, int CK, int D, int GT>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
-  const dim3 grid((unsigned)(a.num_kv_heads * (a.group / GT)), (unsigned)a.num_parts, (unsigned)a.num_seqs);
-  if (a.group > GT)
-    decode_mfma<QK, CK, D, GT, true><<<grid, dim3(kThreads), 0, stream>>>(a);
+  const unsigned columns = (unsigned)(a.num_kv_heads * (a.group / GT));
+  if (a.balanced)
+    launch_s<QK, CK, D, GT, true>(a, dim3(columns, (unsigned)(a.ranges / 4), 1u), stream);
   else
-    decode_mfma<QK, CK, D, GT, false><<<grid, dim3(kThreads), 0, stream>>>(a);
+    launch_s<QK, CK, D, GT, false>(a, dim3(columns, (unsigned)a.num_parts, (unsigned)a.num_seqs), stream);
   return hipGetLastError();
 }
 

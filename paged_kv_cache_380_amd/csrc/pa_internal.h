@@ -34,6 +34,8 @@ struct DecodeArgs {
   const int32_t* context_lens;
   float* ws_out;          // [S, H, P, D] unnormalised partition outputs
   float* ws_ml;           // [S, H, P, 2] partition max (log2 domain) and sum
+                          // (balanced schedule: [H, S + R, D] and [H, S + R, 2], slot s + r)
+  int* ws_pref;           // balanced schedule: [S + 1] first flattened block of each sequence
   float qk_scale;         // scale * log2(e) (* k_scale for FP8 caches)
   float out_scale;        // v_scale for FP8 caches, else 1
   int num_seqs;
@@ -48,6 +50,8 @@ struct DecodeArgs {
   int num_parts;          // ceil(max_blocks / partition_blocks)
   int out_kind;           // Kind of out: F32 or the query kind
   int use_mfma;           // 1: matrix-core kernel (16-bit queries, group_tile 4, 8 or 16)
+  int balanced;           // 1: balanced schedule (matrix-core kernel only): equal block ranges per wave
+  int ranges;             // balanced schedule: number of ranges R (a multiple of 4)
 };
 
 // Queues the decode kernel(s) chosen by a.use_mfma, then the partition merge if needed.
@@ -101,5 +105,8 @@ inline int mfma_group_tile(int group) {
 }
 
 constexpr int kMaxPartitionBlocks = 512;
+
+// Largest batch the balanced schedule serves (its block-count prefix lives in LDS).
+constexpr int kBalancedMaxSeqs = 1024;
 
 }  // namespace pa

@@ -118,13 +118,36 @@ def test_copy_blocks_zero_pairs_is_a_no_op(lib):
 
 
 def test_workspace_checks(lib):
-    # 4 seqs x 2 KV heads = 8 tiles -> split; a workspace is required
+    # 4 seqs x 2 KV heads = 8 tiles -> split; a workspace is required. With the
+    # library's own choice, a workspace too small for the balanced schedule
+    # selects the partitioned one, so "too small" means below what that needs.
     need = lib.pa_decode_workspace_bytes(4, 8, 2, 128, 64, 16, 0)
-    assert need > 0
+    pb = binding.decode_partition_blocks(4, 8, 2, 128, 64)
+    split_need = lib.pa_decode_workspace_bytes(4, 8, 2, 128, 64, 16, pb)
+    assert need >= split_need > 0
     assert decode(lib, M=64) == 5
-    assert decode(lib, M=64, ws=FAKE, wsb=need - 1) == 5
+    assert decode(lib, M=64, ws=FAKE, wsb=split_need - 1) == 5
     assert decode(lib, M=64, ws=FAKE + 4, wsb=need) == 5
+    assert decode(lib, split=pb, M=64, ws=FAKE, wsb=split_need - 1) == 5
     assert "workspace" in lib.pa_last_error().decode()
+
+
+def test_balanced_workspace_bytes(lib):
+    # 64 seqs, 32 heads over 8 KV heads (head tile 4: 8 columns), 256-block rows.
+    # Sized for the larger range count (FP8 caches: 2048 waves / 8 columns =
+    # 256 ranges); per head S + R slots of D floats and of (max, sum), then
+    # S + 1 ints of block prefix, each part 256-byte aligned. The partitioned
+    # schedule needs none here (512 tiles).
+    S, H, Hkv, D, M, R = 64, 32, 8, 128, 256, 256
+    rows = H * (S + R)
+    out_bytes = rows * D * 4
+    ml_off = (out_bytes + 255) // 256 * 256
+    pref_off = (ml_off + rows * 2 * 4 + 255) // 256 * 256
+    assert lib.pa_decode_workspace_bytes(S, H, Hkv, D, M, 16, 0) == pref_off + (S + 1) * 4
+    # no head tile of 4 (group 6): only the partitioned schedule can run
+    assert lib.pa_decode_workspace_bytes(S, 48, 8, D, M, 16, 0) == 0
+    # past the largest balanced batch: only the partitioned schedule
+    assert lib.pa_decode_workspace_bytes(1025, H, Hkv, D, 4, 16, 0) == 0
 
 
 def test_workspace_bytes_formula(lib):
