@@ -674,36 +674,72 @@ __global__ __launch_bounds__(64) void decode_bal_reduce(const DecodeArgs a) {
   const float* ml = a.ws_ml + ((int64_t)h * slots + seq + r_lo) * 2;
   const float* o = a.ws_out + ((int64_t)h * slots + seq + r_lo) * D;
   auto held = [&](int i) { return (int64_t)(r_lo + i) * T / R < (int64_t)(r_lo + i + 1) * T / R; };
-  // Maxima and sums with the lanes across the pieces.
-  float M = kNegInf;
-  for (int i = lane; i < pieces; i += 64)
-    if (held(i)) M = fmaxf(M, ml[2 * i]);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
-  float L = 0.f;
-  for (int i = lane; i < pieces; i += 64)
-    if (held(i)) L += ml[2 * i + 1] * fast_exp2(ml[2 * i] - M);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off, 64);
-  // Outputs: 64 pieces at a time, their weights staged in LDS (0 for ranges
-  // that hold no block; their slots were never written and are skipped by
-  // selection, not multiplied).
   float O[D / 64];
 #pragma unroll
   for (int k = 0; k < D / 64; ++k) O[k] = 0.f;
-  for (int base = 0; base < pieces; base += 64) {
-    const int i = base + lane;
-    wave_lds_fence();
-    s_f[lane] = (i < pieces && held(i)) ? fast_exp2(ml[2 * i] - M) : 0.f;
-    wave_lds_fence();
-    const int n = min(64, pieces - base);
-#pragma unroll 8
-    for (int j = 0; j < n; ++j) {
-      const float f = s_f[j];
+  float M = kNegInf, L = 0.f;
+  if (pieces <= 64) {
+    // Common case, one round of loads: lane i takes piece i's max and sum,
+    // every lane its columns of the first kPre pieces' outputs; the weights
+    // are then shared by lane reads.
+    constexpr int kPre = 8;
+    float ov[kPre][D / 64];
+#pragma unroll
+    for (int j = 0; j < kPre; ++j)
+#pragma unroll
+      for (int k = 0; k < D / 64; ++k) ov[j][k] = j < pieces ? o[(int64_t)j * D + lane + 64 * k] : 0.f;
+    const bool mine = lane < pieces && held(lane);
+    const float m = mine ? ml[2 * lane] : kNegInf;
+    const float l = mine ? ml[2 * lane + 1] : 0.f;
+    M = m;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+    const float f = mine ? fast_exp2(m - M) : 0.f;
+    L = l * f;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off, 64);
+#pragma unroll
+    for (int j = 0; j < kPre; ++j) {
+      const float fj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), j));
+#pragma unroll
+      for (int k = 0; k < D / 64; ++k) O[k] += fj != 0.f ? ov[j][k] * fj : 0.f;
+    }
+#pragma unroll 4
+    for (int j = kPre; j < pieces; ++j) {
+      const float fj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), j));
 #pragma unroll
       for (int k = 0; k < D / 64; ++k) {
-        const float v = o[(int64_t)(base + j) * D + lane + 64 * k];
-        O[k] += f != 0.f ? v * f : 0.f;
+        const float v = o[(int64_t)j * D + lane + 64 * k];
+        O[k] += fj != 0.f ? v * fj : 0.f;
+      }
+    }
+  } else {
+    // Maxima and sums with the lanes across the pieces.
+    for (int i = lane; i < pieces; i += 64)
+      if (held(i)) M = fmaxf(M, ml[2 * i]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+    for (int i = lane; i < pieces; i += 64)
+      if (held(i)) L += ml[2 * i + 1] * fast_exp2(ml[2 * i] - M);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off, 64);
+    // Outputs: 64 pieces at a time, their weights staged in LDS (0 for ranges
+    // that hold no block; their slots were never written and are skipped by
+    // selection, not multiplied).
+    for (int base = 0; base < pieces; base += 64) {
+      const int i = base + lane;
+      wave_lds_fence();
+      s_f[lane] = (i < pieces && held(i)) ? fast_exp2(ml[2 * i] - M) : 0.f;
+      wave_lds_fence();
+      const int n = min(64, pieces - base);
+#pragma unroll 8
+      for (int j = 0; j < n; ++j) {
+        const float f = s_f[j];
+#pragma unroll
+        for (int k = 0; k < D / 64; ++k) {
+          const float v = o[(int64_t)(base + j) * D + lane + 64 * k];
+          O[k] += f != 0.f ? v * f : 0.f;
+        }
       }
     }
   }
