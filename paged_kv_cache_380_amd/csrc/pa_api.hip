@@ -85,13 +85,22 @@ struct Layout {
 constexpr int kBalancedWaves16 = 1024;
 constexpr int kBalancedWavesFp8 = 2048;
 
+// Query heads per wave in the balanced schedule: 32 (two 16-head sub-tiles
+// sharing every K/V tile) for groups of 64 or more, else the matrix-core
+// tile. Measured at 32 heads over one KV head, two 16-head waves sharing
+// K/V through L2 beat one 32-head wave (its registers leave one wave per
+// SIMD, which cannot overlap its arithmetic with its loads); from 64 heads
+// on, reading K/V once per 32 heads wins.
+int balanced_tile(int group) { return group % 32 == 0 && group >= 64 ? 32 : pa::mfma_group_tile(group); }
+
 bool balanced_fits(int num_seqs, int max_blocks) {
   return num_seqs <= pa::kBalancedMaxSeqs && (int64_t)num_seqs * max_blocks <= 0x7fffffffLL;
 }
 
 int64_t balanced_ranges(int num_heads, int group_tile, bool fp8_cache) {
   const int64_t columns = num_heads / group_tile;
-  const int64_t waves = fp8_cache ? kBalancedWavesFp8 : kBalancedWaves16;
+  // A 32-head tile holds more than 256 registers: one wave per SIMD whatever the cache.
+  const int64_t waves = fp8_cache && group_tile <= 16 ? kBalancedWavesFp8 : kBalancedWaves16;
   const int64_t r = (waves + columns - 1) / columns;
   return (r + 3) / 4 * 4;
 }
@@ -248,7 +257,7 @@ size_t pa_decode_workspace_bytes(int num_seqs, int num_heads, int num_kv_heads, 
     // The kernel family depends on the query dtype and the balanced range
     // count on the cache dtype, neither of which this function sees: size for
     // the largest need the choice may have (FP8's range count is the larger).
-    const int tile = pa::mfma_group_tile(num_heads / num_kv_heads);
+    const int tile = balanced_tile(num_heads / num_kv_heads);
     if (tile && balanced_fits(num_seqs, max_blocks_per_seq) && num_seqs > 0)
       balanced = balanced_layout(num_seqs, num_heads, head_size,
                                  balanced_ranges(num_heads, tile, /*fp8_cache=*/true)).total;
@@ -302,7 +311,7 @@ int pa_decode_split(void* out, const void* q, const void* k_cache, const void* v
   // It needs a workspace; a caller that passes none (or too small a one, as
   // sized before this schedule existed) gets the partitioned schedule.
   bool balanced = partition_blocks == 0 && mfma && balanced_fits(num_seqs, max_blocks_per_seq);
-  const int64_t ranges = balanced ? balanced_ranges(num_heads, group_tile, fp8) : 0;
+  const int64_t ranges = balanced ? balanced_ranges(num_heads, balanced_tile(group), fp8) : 0;
   if (balanced && (!workspace || workspace_bytes < balanced_layout(num_seqs, num_heads, head_size, ranges).total))
     balanced = false;
   if (ranges / 4 > 65535) return fail(PA_ERR_UNSUPPORTED, "decode: too many ranges (%lld)", (long long)ranges);
@@ -340,7 +349,7 @@ int pa_decode_split(void* out, const void* q, const void* k_cache, const void* v
   a.head_size = head_size;
   a.group = group;
   a.use_mfma = mfma ? 1 : 0;
-  a.group_tile = group_tile;
+  a.group_tile = balanced ? balanced_tile(group) : group_tile;
   a.balanced = balanced ? 1 : 0;
   a.ranges = balanced ? (int)ranges : 0;
   a.num_blocks = num_blocks;

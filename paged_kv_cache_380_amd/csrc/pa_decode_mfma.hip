@@ -57,6 +57,7 @@ namespace {
 constexpr float kSlack = 8.0f;    // lazy-max slack, log2 units
 constexpr int kRing = 2;          // register ring depth: blocks per wave in flight, plus the one in use
 constexpr int kRingBalanced = 2;  // the same for the balanced schedule
+constexpr int kRingWide = 2;      // the same for 32-head tiles (one wave per SIMD)
 
 // Geometry of one (block, KV head) tile for the MFMA kernel.
 template <int CK, int D> struct MGeo {
@@ -107,7 +108,10 @@ __global__ __launch_bounds__(kThreads) void decode_mfma(const DecodeArgs a) {
   using G = MGeo<CK, D>;
   constexpr int NKB = G::NKB, NKL = G::NKL, NVL = G::NVL, NDB = G::NDB, VS = G::kVStride;
   static_assert(QK == kF16 || QK == kBF16, "16-bit queries");
-  static_assert(GT == 4 || GT == 8 || GT == 16, "head tile of 4, 8 or 16");
+  static_assert(GT == 4 || GT == 8 || GT == 16 || (GT == 32 && kBalanced),
+                "head tile of 4, 8 or 16; 32 (two sub-tiles per wave) in the balanced schedule only");
+  constexpr int NT = GT > 16 ? GT / 16 : 1;  // 16-head sub-tiles of a wave, sharing each K/V tile
+  constexpr int GS = GT > 16 ? 16 : GT;      // heads per sub-tile
 
   __shared__ int s_blocks[kMaxPartitionBlocks];
   __shared__ __align__(16) uint16_t s_v[kWaves][16 * VS];
@@ -131,30 +135,37 @@ __global__ __launch_bounds__(kThreads) void decode_mfma(const DecodeArgs a) {
   int blk0 = 0;    // its first block handled here (partition start, or start of the piece)
   int sb_off = 0;  // entry of s_blocks holding block blk0
 
-  // q as the B operand of S = K·Qᵀ: lane (n, g) holds head h0 + n, the 8
-  // elements of k block b that group g supplies; heads past the tile are zero.
-  uint32_t qf[NKB][4];
+  // q as the B operand of S = K·Qᵀ: for sub-tile t, lane (n, g) holds head
+  // h0 + 16t + n, the 8 elements of k block b that group g supplies; heads
+  // past the tile are zero.
+  uint32_t qf[NT][NKB][4];
   auto load_q = [&](int s) {
-    const char* qp = static_cast<const char*>(a.q) + ((int64_t)s * a.num_heads + h0 + n) * D * 2;
 #pragma unroll
-    for (int b = 0; b < NKB; ++b) {
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (n < GT) v = *reinterpret_cast<const uint4*>(qp + k_col<CK>(b, g) * 2);
-      qf[b][0] = v.x;
-      qf[b][1] = v.y;
-      qf[b][2] = v.z;
-      qf[b][3] = v.w;
+    for (int t = 0; t < NT; ++t) {
+      const char* qp = static_cast<const char*>(a.q) + ((int64_t)s * a.num_heads + h0 + 16 * t + n) * D * 2;
+#pragma unroll
+      for (int b = 0; b < NKB; ++b) {
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (n < GS) v = *reinterpret_cast<const uint4*>(qp + k_col<CK>(b, g) * 2);
+        qf[t][b][0] = v.x;
+        qf[t][b][1] = v.y;
+        qf[t][b][2] = v.z;
+        qf[t][b][3] = v.w;
+      }
     }
   };
 
-  f32x4_t acc[NDB];
-  float mref;  // running reference max of head n (log2 units), equal on lanes n, n+16, n+32, n+48
-  float lsum;  // this lane's share of the running sum of head n
+  f32x4_t acc[NT][NDB];
+  float mref[NT];  // running reference max of head n (log2 units), equal on lanes n, n+16, n+32, n+48
+  float lsum[NT];  // this lane's share of the running sum of head n
   auto reset = [&]() {
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) acc[db] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-    mref = kNegInf;
-    lsum = 0.f;
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) acc[t][db] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+      mref[t] = kNegInf;
+      lsum[t] = 0.f;
+    }
   };
 
   const int64_t blk_stride = (int64_t)a.num_kv_heads * G::kTileBytes;
@@ -211,8 +222,10 @@ __global__ __launch_bounds__(kThreads) void decode_mfma(const DecodeArgs a) {
       }
     }
 
-    // S = K·Qᵀ: lane (n, g) ends with the logits of head n for tokens 4g + i.
-    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+    // S = K·Qᵀ per sub-tile: lane (n, g) ends with the logits of head n for tokens 4g + i.
+    f32x4_t sc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) sc[t] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
     if constexpr (CK == kFP8) {
 #pragma unroll
       for (int c = 0; c < NKL; ++c) {
@@ -221,57 +234,69 @@ __global__ __launch_bounds__(kThreads) void decode_mfma(const DecodeArgs a) {
         fp8x4_to_16<QK>(kr[c].y, w[2], w[3]);
         fp8x4_to_16<QK>(kr[c].z, w[4], w[5]);
         fp8x4_to_16<QK>(kr[c].w, w[6], w[7]);
-        s = mma_k32<QK>(w, qf[2 * c], s);
-        s = mma_k32<QK>(w + 4, qf[2 * c + 1], s);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          sc[t] = mma_k32<QK>(w, qf[t][2 * c], sc[t]);
+          sc[t] = mma_k32<QK>(w + 4, qf[t][2 * c + 1], sc[t]);
+        }
       }
     } else {
 #pragma unroll
       for (int c = 0; c < NKL; ++c) {
         const uint32_t w[4] = {kr[c].x, kr[c].y, kr[c].z, kr[c].w};
-        s = mma_k32<QK>(w, qf[c], s);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) sc[t] = mma_k32<QK>(w, qf[t][c], sc[t]);
       }
     }
 
-    float x[4];
+    // Online softmax per sub-tile; P as hi + lo in the 16-bit type (the A
+    // operand: head n, tokens 4g .. 4g+3).
+    uint32_t ph[NT][2], pl[NT][2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[i] = s[i] * qk_scale;
-      if (n >= GT || (kMasked && 4 * g + i >= valid)) x[i] = kNegInf;
-    }
-    const float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    if (__builtin_amdgcn_ballot_w64(bm > mref + kSlack) != 0) {  // raise the reference max (wave-uniform)
-      float bmx = fmaxf(bm, __shfl_xor(bm, 16, 64));
-      bmx = fmaxf(bmx, __shfl_xor(bmx, 32, 64));
-      const float mn = fmaxf(mref, bmx);
-      const float alpha = fast_exp2(mref - ((mn == kNegInf) ? 0.f : mn));
-      lsum *= alpha;
-      mref = mn;
+    for (int t = 0; t < NT; ++t) {
+      float x[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float al = __shfl(alpha, 4 * g + i, 64);  // the factor of head 4g + i (rows of acc)
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) acc[db][i] *= al;
+        x[i] = sc[t][i] * qk_scale;
+        if (n >= GS || (kMasked && 4 * g + i >= valid)) x[i] = kNegInf;
       }
-    }
-    const float ms = (mref == kNegInf) ? 0.f : mref;
-    float p[4];
+      const float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      if (__builtin_amdgcn_ballot_w64(bm > mref[t] + kSlack) != 0) {  // raise the reference max (wave-uniform)
+        float bmx = fmaxf(bm, __shfl_xor(bm, 16, 64));
+        bmx = fmaxf(bmx, __shfl_xor(bmx, 32, 64));
+        const float mn = fmaxf(mref[t], bmx);
+        const float alpha = fast_exp2(mref[t] - ((mn == kNegInf) ? 0.f : mn));
+        lsum[t] *= alpha;
+        mref[t] = mn;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[i] = fast_exp2(x[i] - ms);
-      lsum += p[i];
+        for (int i = 0; i < 4; ++i) {
+          const float al = __shfl(alpha, 4 * g + i, 64);  // the factor of head 4g + i (rows of acc)
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) acc[t][db][i] *= al;
+        }
+      }
+      const float ms = (mref[t] == kNegInf) ? 0.f : mref[t];
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[i] = fast_exp2(x[i] - ms);
+        lsum[t] += p[i];
+      }
+      ph[t][0] = pack2<QK>(p[0], p[1]);
+      ph[t][1] = pack2<QK>(p[2], p[3]);
+      pl[t][0] = pack2<QK>(p[0] - lo16_to_f32<QK>(ph[t][0]), p[1] - hi16_to_f32<QK>(ph[t][0]));
+      pl[t][1] = pack2<QK>(p[2] - lo16_to_f32<QK>(ph[t][1]), p[3] - hi16_to_f32<QK>(ph[t][1]));
     }
-    // P as hi + lo in the 16-bit type (the A operand: head n, tokens 4g .. 4g+3).
-    const uint32_t h01 = pack2<QK>(p[0], p[1]);
-    const uint32_t h23 = pack2<QK>(p[2], p[3]);
-    const uint32_t l01 = pack2<QK>(p[0] - lo16_to_f32<QK>(h01), p[1] - hi16_to_f32<QK>(h01));
-    const uint32_t l23 = pack2<QK>(p[2] - lo16_to_f32<QK>(h23), p[3] - hi16_to_f32<QK>(h23));
 
     wave_lds_fence();  // the staged V tile is written
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       const u32x2_t b = v_operand_tr(sv, VS, db * 16, lane);
-      acc[db] = mma_k16<QK>(h01, h23, b[0], b[1], acc[db]);
-      acc[db] = mma_k16<QK>(l01, l23, b[0], b[1], acc[db]);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        acc[t][db] = mma_k16<QK>(ph[t][0], ph[t][1], b[0], b[1], acc[t][db]);
+        acc[t][db] = mma_k16<QK>(pl[t][0], pl[t][1], b[0], b[1], acc[t][db]);
+      }
     }
   };
 
@@ -290,7 +315,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma(const DecodeArgs a) {
       // after its last.
       Tile tm;
       if (tail_masked) load_tile(n_full, tm);
-      stream_blocks<kRingBalanced, Tile>(0, 1, n_full, load_tile,
+      stream_blocks<(NT > 1 ? kRingWide : kRingBalanced), Tile>(0, 1, n_full, load_tile,
                                          [&](int j, const Tile& t) { process(std::false_type{}, j, t); });
       if (tail_masked) process(std::true_type{}, n_full, tm);
     } else {
@@ -326,17 +351,17 @@ __global__ __launch_bounds__(kThreads) void decode_mfma(const DecodeArgs a) {
     run_blocks(wave, kWaves, nblk, seq_blocks);
 
     // This wave's sum of head n over its four row groups; the max is already shared.
-    lsum += __shfl_xor(lsum, 16, 64);
-    lsum += __shfl_xor(lsum, 32, 64);
+    float ls = lsum[0] + __shfl_xor(lsum[0], 16, 64);
+    ls += __shfl_xor(ls, 32, 64);
     if (g == 0 && n < GT) {
-      s_ml[(wave * GT + n) * 2] = mref;
-      s_ml[(wave * GT + n) * 2 + 1] = lsum;
+      s_ml[(wave * GT + n) * 2] = mref[0];
+      s_ml[(wave * GT + n) * 2 + 1] = ls;
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (4 * g + i < GT) {
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) s_acc[(wave * GT + 4 * g + i) * D + db * 16 + n] = acc[db][i];
+        for (int db = 0; db < NDB; ++db) s_acc[(wave * GT + 4 * g + i) * D + db * 16 + n] = acc[0][db][i];
       }
     }
     __syncthreads();
@@ -443,35 +468,40 @@ __global__ __launch_bounds__(kThreads) void decode_mfma(const DecodeArgs a) {
         sub = sub_end;
       }
 
-      float ls = lsum + __shfl_xor(lsum, 16, 64);
-      ls += __shfl_xor(ls, 32, 64);
-      if (pos == ps && piece_end == pe) {
-        // The whole sequence: normalise and write the output rows 4g + i.
-        float inv[4];
+      const bool whole = pos == ps && piece_end == pe;
+      const int64_t slot = seq + r;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) inv[i] = a.out_scale / __shfl(ls, 4 * g + i, 64);
+      for (int t = 0; t < NT; ++t) {
+        float ls = lsum[t] + __shfl_xor(lsum[t], 16, 64);
+        ls += __shfl_xor(ls, 32, 64);
+        const int hb = h0 + 16 * t;  // first head of the sub-tile
+        if (whole) {
+          // The whole sequence: normalise and write the output rows 4g + i.
+          float inv[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (4 * g + i < GT) {
-            const int64_t row = ((int64_t)seq * a.num_heads + h0 + 4 * g + i) * D;
+          for (int i = 0; i < 4; ++i) inv[i] = a.out_scale / __shfl(ls, 4 * g + i, 64);
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) store_out(a, row + db * 16 + n, acc[db][i] * inv[i]);
+          for (int i = 0; i < 4; ++i) {
+            if (4 * g + i < GS) {
+              const int64_t row = ((int64_t)seq * a.num_heads + hb + 4 * g + i) * D;
+#pragma unroll
+              for (int db = 0; db < NDB; ++db) store_out(a, row + db * 16 + n, acc[t][db][i] * inv[i]);
+            }
           }
-        }
-      } else {
-        const int64_t slot = seq + r;
+        } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (4 * g + i < GT) {
-            float* o = a.ws_out + ((int64_t)(h0 + 4 * g + i) * slots + slot) * D;
+          for (int i = 0; i < 4; ++i) {
+            if (4 * g + i < GS) {
+              float* o = a.ws_out + ((int64_t)(hb + 4 * g + i) * slots + slot) * D;
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) o[db * 16 + n] = acc[db][i] * a.out_scale;
+              for (int db = 0; db < NDB; ++db) o[db * 16 + n] = acc[t][db][i] * a.out_scale;
+            }
           }
-        }
-        if (g == 0 && n < GT) {
-          float* ml = a.ws_ml + ((int64_t)(h0 + n) * slots + slot) * 2;
-          ml[0] = mref;
-          ml[1] = ls;
+          if (g == 0 && n < GS) {
+            float* ml = a.ws_ml + ((int64_t)(hb + n) * slots + slot) * 2;
+            ml[0] = mref[t];
+            ml[1] = ls;
+          }
         }
       }
       pos = piece_end;
@@ -490,10 +520,12 @@ void launch_s(const DecodeArgs& a, dim3 grid, hipStream_t stream) {
 template <int QK, int CK, int D, int GT>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
   const unsigned columns = (unsigned)(a.num_kv_heads * (a.group / GT));
-  if (a.balanced)
+  if (a.balanced) {
     launch_s<QK, CK, D, GT, true>(a, dim3(columns, (unsigned)(a.ranges / 4), 1u), stream);
-  else
-    launch_s<QK, CK, D, GT, false>(a, dim3(columns, (unsigned)a.num_parts, (unsigned)a.num_seqs), stream);
+  } else {
+    if constexpr (GT > 16) return hipErrorInvalidValue;  // 32-head tiles exist in the balanced schedule only
+    else launch_s<QK, CK, D, GT, false>(a, dim3(columns, (unsigned)a.num_parts, (unsigned)a.num_seqs), stream);
+  }
   return hipGetLastError();
 }
 
@@ -503,6 +535,7 @@ hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
     case 4: return launch_t<QK, CK, D, 4>(a, stream);
     case 8: return launch_t<QK, CK, D, 8>(a, stream);
     case 16: return launch_t<QK, CK, D, 16>(a, stream);
+    case 32: return launch_t<QK, CK, D, 32>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

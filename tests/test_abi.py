@@ -144,6 +144,13 @@ def test_balanced_workspace_bytes(lib):
     ml_off = (out_bytes + 255) // 256 * 256
     pref_off = (ml_off + rows * 2 * 4 + 255) // 256 * 256
     assert lib.pa_decode_workspace_bytes(S, H, Hkv, D, M, 16, 0) == pref_off + (S + 1) * 4
+    # 64 query heads over one KV head: 32-head tiles, two columns, R = 512 ranges
+    # (a 32-head tile runs one wave per SIMD, so no FP8 doubling)
+    rows = 64 * (S + 512)
+    out_bytes = rows * D * 4
+    ml_off = (out_bytes + 255) // 256 * 256
+    pref_off = (ml_off + rows * 2 * 4 + 255) // 256 * 256
+    assert lib.pa_decode_workspace_bytes(S, 64, 1, D, M, 16, 0) == pref_off + (S + 1) * 4
     # no head tile of 4 (group 6): only the partitioned schedule can run
     assert lib.pa_decode_workspace_bytes(S, 48, 8, D, M, 16, 0) == 0
     # past the largest balanced batch: only the partitioned schedule

@@ -8,7 +8,10 @@ cases here aim at that cutting: many sequences shorter than a range, empty
 sequences between them, one sequence spanning many ranges, far fewer blocks
 than ranges, the largest batch the schedule serves and the first one past it
 (which takes the partitioned schedule). Each is checked against the oracle on
-every sequence, against the partitioned schedule, and for determinism.
+every sequence, against the partitioned schedule, and for determinism. A
+group of 64 query heads per KV head runs with 32 heads per wave (two 16-head
+sub-tiles sharing each K/V tile), two waves per KV head; a group of 32 runs
+as two 16-head waves.
 """
 
 import zlib
@@ -55,7 +58,7 @@ KINDS = ["short_and_empty", "one_long_many_short", "fewer_blocks_than_ranges", "
 
 @pytest.mark.parametrize("kind", KINDS)
 @pytest.mark.parametrize("H,Hkv,dtype,cache", [(8, 2, "bf16", "bf16"), (32, 1, "f16", "f16"),
-                                               (16, 4, "bf16", "fp8_e4m3")])
+                                               (16, 4, "bf16", "fp8_e4m3"), (64, 1, "bf16", "fp8_e4m3")])
 def test_balanced_against_oracle(kind, H, Hkv, dtype, cache):
     rng = np.random.default_rng(zlib.crc32(f"{kind}/{H}".encode()))
     lens = lens_for(kind, rng)
