@@ -114,7 +114,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma(const DecodeArgs a) {
   constexpr int GS = GT > 16 ? 16 : GT;      // heads per sub-tile
 
   __shared__ int s_blocks[kMaxPartitionBlocks];
-  __shared__ __align__(16) uint16_t s_v[kWaves][16 * VS];
+  __shared__ __align__(16) uint16_t s_v[kWaves][2 * 16 * VS];  // two staged V tiles per wave
   __shared__ float s_acc[kBalanced ? 1 : kWaves * GT * D];
   __shared__ float s_ml[kBalanced ? 1 : kWaves * GT * 2];
   __shared__ int s_pref[kBalanced ? kBalancedMaxSeqs + 1 : 1];
@@ -192,75 +192,96 @@ __global__ __launch_bounds__(kThreads) void decode_mfma(const DecodeArgs a) {
     for (int c = 0; c < NVL; ++c) vr[c] = load_kv<kShared>(vt + v_off + c * 1024);
   };
 
-  auto process = [&](auto masked, int j, const Tile& t) {
+  // One step over NP (1 or 2) tiles t0, t1 holding valid0, valid1 token rows
+  // inside the context (16 unless kMasked; 0 marks a missing second tile,
+  // whose registers are then t0's and are never used unmasked). With two
+  // tiles the P·V products take both at once: the 32 tokens of a 16x16x32
+  // MFMA are this lane group's four rows of t0 followed by its four rows of
+  // t1 (a contraction does not care about the order of its terms), which
+  // halves the P·V instructions and gives the softmax two independent chains.
+  auto process = [&](auto masked, auto np_c, const Tile& t0, const Tile& t1, int valid0, int valid1) {
     constexpr bool kMasked = decltype(masked)::value;
-    const uint4(&kr)[NKL] = t.k;
-    const uint4(&vr)[NVL] = t.v;
-    const int valid = kMasked ? ctx - (blk0 + j) * 16 : 16;  // token rows of this block inside the context
+    constexpr int NP = decltype(np_c)::value;
+    const Tile* tl[2] = {&t0, &t1};
+    const int valid[2] = {kMasked ? valid0 : 16, kMasked ? valid1 : 16};
 
     // Stage V (row-major, 16-bit) for the transposed operand reads.
-    wave_lds_fence();  // the previous block's reads of sv are issued before it is overwritten
+    wave_lds_fence();  // the previous step's reads of sv are issued before it is overwritten
 #pragma unroll
-    for (int c = 0; c < NVL; ++c) {
-      const int byte = c * 1024 + lane * 16;
-      const int row = byte / G::kRowBytes;
-      const int col = (byte % G::kRowBytes) / G::kBytes;
-      const bool keep = !kMasked || row < valid;
-      uint4 v = vr[c];
-      if constexpr (CK == kFP8) {
-        uint4 w0, w1;
-        fp8x4_to_16<QK>(v.x, w0.x, w0.y);
-        fp8x4_to_16<QK>(v.y, w0.z, w0.w);
-        fp8x4_to_16<QK>(v.z, w1.x, w1.y);
-        fp8x4_to_16<QK>(v.w, w1.z, w1.w);
-        if (!keep) w0 = w1 = make_uint4(0u, 0u, 0u, 0u);
-        *reinterpret_cast<uint4*>(sv + row * VS + col) = w0;
-        *reinterpret_cast<uint4*>(sv + row * VS + col + 8) = w1;
-      } else {
-        if (!keep) v = make_uint4(0u, 0u, 0u, 0u);
-        *reinterpret_cast<uint4*>(sv + row * VS + col) = v;
+    for (int p = 0; p < NP; ++p) {
+      uint16_t* svp = sv + p * 16 * VS;
+#pragma unroll
+      for (int c = 0; c < NVL; ++c) {
+        const int byte = c * 1024 + lane * 16;
+        const int row = byte / G::kRowBytes;
+        const int col = (byte % G::kRowBytes) / G::kBytes;
+        const bool keep = !kMasked || row < valid[p];
+        uint4 v = tl[p]->v[c];
+        if constexpr (CK == kFP8) {
+          uint4 w0, w1;
+          fp8x4_to_16<QK>(v.x, w0.x, w0.y);
+          fp8x4_to_16<QK>(v.y, w0.z, w0.w);
+          fp8x4_to_16<QK>(v.z, w1.x, w1.y);
+          fp8x4_to_16<QK>(v.w, w1.z, w1.w);
+          if (!keep) w0 = w1 = make_uint4(0u, 0u, 0u, 0u);
+          *reinterpret_cast<uint4*>(svp + row * VS + col) = w0;
+          *reinterpret_cast<uint4*>(svp + row * VS + col + 8) = w1;
+        } else {
+          if (!keep) v = make_uint4(0u, 0u, 0u, 0u);
+          *reinterpret_cast<uint4*>(svp + row * VS + col) = v;
+        }
       }
     }
 
-    // S = K·Qᵀ per sub-tile: lane (n, g) ends with the logits of head n for tokens 4g + i.
-    f32x4_t sc[NT];
+    // S = K·Qᵀ per sub-tile and tile: lane (n, g) ends with the logits of head
+    // n for tokens 4g + i.
+    f32x4_t sc[NT][NP];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) sc[t] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-    if constexpr (CK == kFP8) {
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int c = 0; c < NKL; ++c) {
-        uint32_t w[8];
-        fp8x4_to_16<QK>(kr[c].x, w[0], w[1]);
-        fp8x4_to_16<QK>(kr[c].y, w[2], w[3]);
-        fp8x4_to_16<QK>(kr[c].z, w[4], w[5]);
-        fp8x4_to_16<QK>(kr[c].w, w[6], w[7]);
+      for (int p = 0; p < NP; ++p) sc[t][p] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          sc[t] = mma_k32<QK>(w, qf[t][2 * c], sc[t]);
-          sc[t] = mma_k32<QK>(w + 4, qf[t][2 * c + 1], sc[t]);
+    for (int p = 0; p < NP; ++p) {
+      const uint4(&kr)[NKL] = tl[p]->k;
+      if constexpr (CK == kFP8) {
+#pragma unroll
+        for (int c = 0; c < NKL; ++c) {
+          uint32_t w[8];
+          fp8x4_to_16<QK>(kr[c].x, w[0], w[1]);
+          fp8x4_to_16<QK>(kr[c].y, w[2], w[3]);
+          fp8x4_to_16<QK>(kr[c].z, w[4], w[5]);
+          fp8x4_to_16<QK>(kr[c].w, w[6], w[7]);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            sc[t][p] = mma_k32<QK>(w, qf[t][2 * c], sc[t][p]);
+            sc[t][p] = mma_k32<QK>(w + 4, qf[t][2 * c + 1], sc[t][p]);
+          }
         }
-      }
-    } else {
+      } else {
 #pragma unroll
-      for (int c = 0; c < NKL; ++c) {
-        const uint32_t w[4] = {kr[c].x, kr[c].y, kr[c].z, kr[c].w};
+        for (int c = 0; c < NKL; ++c) {
+          const uint32_t w[4] = {kr[c].x, kr[c].y, kr[c].z, kr[c].w};
 #pragma unroll
-        for (int t = 0; t < NT; ++t) sc[t] = mma_k32<QK>(w, qf[t][c], sc[t]);
+          for (int t = 0; t < NT; ++t) sc[t][p] = mma_k32<QK>(w, qf[t][c], sc[t][p]);
+        }
       }
     }
 
     // Online softmax per sub-tile; P as hi + lo in the 16-bit type (the A
-    // operand: head n, tokens 4g .. 4g+3).
-    uint32_t ph[NT][2], pl[NT][2];
+    // operand: head n, tokens 4g .. 4g+3 of each tile).
+    uint32_t ph[NT][NP][2], pl[NT][NP][2];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      float x[4];
+      float x[NP][4];
+      float bm = kNegInf;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[i] = sc[t][i] * qk_scale;
-        if (n >= GS || (kMasked && 4 * g + i >= valid)) x[i] = kNegInf;
-      }
-      const float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      for (int p = 0; p < NP; ++p)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[p][i] = sc[t][p][i] * qk_scale;
+          if (n >= GS || (kMasked && 4 * g + i >= valid[p])) x[p][i] = kNegInf;
+          bm = fmaxf(bm, x[p][i]);
+        }
       if (__builtin_amdgcn_ballot_w64(bm > mref[t] + kSlack) != 0) {  // raise the reference max (wave-uniform)
         float bmx = fmaxf(bm, __shfl_xor(bm, 16, 64));
         bmx = fmaxf(bmx, __shfl_xor(bmx, 32, 64));
@@ -276,55 +297,94 @@ __global__ __launch_bounds__(kThreads) void decode_mfma(const DecodeArgs a) {
         }
       }
       const float ms = (mref[t] == kNegInf) ? 0.f : mref[t];
-      float p[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[i] = fast_exp2(x[i] - ms);
-        lsum[t] += p[i];
+      for (int p = 0; p < NP; ++p) {
+        float pr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pr[i] = fast_exp2(x[p][i] - ms);
+          lsum[t] += pr[i];
+        }
+        ph[t][p][0] = pack2<QK>(pr[0], pr[1]);
+        ph[t][p][1] = pack2<QK>(pr[2], pr[3]);
+        pl[t][p][0] = pack2<QK>(pr[0] - lo16_to_f32<QK>(ph[t][p][0]), pr[1] - hi16_to_f32<QK>(ph[t][p][0]));
+        pl[t][p][1] = pack2<QK>(pr[2] - lo16_to_f32<QK>(ph[t][p][1]), pr[3] - hi16_to_f32<QK>(ph[t][p][1]));
       }
-      ph[t][0] = pack2<QK>(p[0], p[1]);
-      ph[t][1] = pack2<QK>(p[2], p[3]);
-      pl[t][0] = pack2<QK>(p[0] - lo16_to_f32<QK>(ph[t][0]), p[1] - hi16_to_f32<QK>(ph[t][0]));
-      pl[t][1] = pack2<QK>(p[2] - lo16_to_f32<QK>(ph[t][1]), p[3] - hi16_to_f32<QK>(ph[t][1]));
     }
 
-    wave_lds_fence();  // the staged V tile is written
+    wave_lds_fence();  // the staged V tiles are written
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const u32x2_t b = v_operand_tr(sv, VS, db * 16, lane);
+      if constexpr (NP == 2) {
+        const u32x2_t b0 = v_operand_tr(sv, VS, db * 16, lane);
+        const u32x2_t b1 = v_operand_tr(sv + 16 * VS, VS, db * 16, lane);
+        const uint32_t b[4] = {b0[0], b0[1], b1[0], b1[1]};
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        acc[t][db] = mma_k16<QK>(ph[t][0], ph[t][1], b[0], b[1], acc[t][db]);
-        acc[t][db] = mma_k16<QK>(pl[t][0], pl[t][1], b[0], b[1], acc[t][db]);
+        for (int t = 0; t < NT; ++t) {
+          const uint32_t ah[4] = {ph[t][0][0], ph[t][0][1], ph[t][1][0], ph[t][1][1]};
+          const uint32_t al[4] = {pl[t][0][0], pl[t][0][1], pl[t][1][0], pl[t][1][1]};
+          acc[t][db] = mma_k32<QK>(ah, b, acc[t][db]);
+          acc[t][db] = mma_k32<QK>(al, b, acc[t][db]);
+        }
+      } else {
+        const u32x2_t b = v_operand_tr(sv, VS, db * 16, lane);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          acc[t][db] = mma_k16<QK>(ph[t][0][0], ph[t][0][1], b[0], b[1], acc[t][db]);
+          acc[t][db] = mma_k16<QK>(pl[t][0][0], pl[t][0][1], b[0], b[1], acc[t][db]);
+        }
       }
     }
   };
 
+  struct Pair {
+    Tile a, b;
+  };
+  using One = std::integral_constant<int, 1>;
+  using Two = std::integral_constant<int, 2>;
+
   // Blocks blk0 + first, blk0 + first + step, ... below blk0 + nblk of a
-  // sequence holding seq_blocks blocks. The block holding rows past the
-  // context (the last of the sequence, when its length is not a multiple of
-  // 16) runs after the steady stream, by the wave that owns it, so the
-  // stream's loop body holds one unmasked block per ring slot and the
-  // accumulators stay in place across iterations.
+  // sequence holding seq_blocks blocks, two per step. The last step is run
+  // apart, by the wave that owns it: the block holding rows past the context
+  // (the last of the sequence, when its length is not a multiple of 16)
+  // and/or a block left without a partner, so the stream's loop body holds
+  // one unmasked pair per ring slot and the accumulators stay in place.
   auto run_blocks = [&](int first, int step, int nblk, int seq_blocks) {
+    if (first >= nblk) return;
     const bool tail_masked = (ctx & 15) && blk0 + nblk == seq_blocks;
-    const int n_full = nblk - (tail_masked ? 1 : 0);
+    const int cnt = (nblk - 1 - first) / step + 1;  // blocks of this wave
+    const bool own_masked = tail_masked && (nblk - 1 - first) % step == 0;
+    const int fin = own_masked ? 2 - (cnt & 1) : (cnt & 1);  // blocks of the last step
+    const int pairs = (cnt - fin) / 2;
+    const int j_fin = first + step * (cnt - fin);            // first block of the last step
+    auto valid_of = [&](int j) { return min(16, ctx - (blk0 + j) * 16); };
+    auto load_pair = [&](int q, Pair& pr) {
+      load_tile(first + step * (2 * q), pr.a);
+      load_tile(first + step * (2 * q + 1), pr.b);
+    };
+    auto proc_pair = [&](int, const Pair& pr) { process(std::false_type{}, Two{}, pr.a, pr.b, 16, 16); };
+    auto run_fin = [&](const Pair& pr) {
+      if (fin == 2)
+        process(std::true_type{}, Two{}, pr.a, pr.b, valid_of(j_fin), valid_of(j_fin + step));
+      else if (fin == 1)
+        process(std::true_type{}, One{}, pr.a, pr.a, valid_of(j_fin), 0);
+    };
     if constexpr (kBalanced) {
-      // One wave per piece, registers to spare: the masked block's loads go
-      // out first, so they arrive with the stream's first block instead of
-      // after its last.
-      Tile tm;
-      if (tail_masked) load_tile(n_full, tm);
-      stream_blocks<(NT > 1 ? kRingWide : kRingBalanced), Tile>(0, 1, n_full, load_tile,
-                                         [&](int j, const Tile& t) { process(std::false_type{}, j, t); });
-      if (tail_masked) process(std::true_type{}, n_full, tm);
+      // One wave per piece, registers to spare: the last step's loads go out
+      // first, so they arrive with the stream's first pair instead of after
+      // its last.
+      Pair fp;
+      if (fin >= 1) load_tile(j_fin, fp.a);
+      if (fin == 2) load_tile(j_fin + step, fp.b);
+      stream_blocks<(NT > 1 ? kRingWide : kRingBalanced), Pair>(0, 1, pairs, load_pair, proc_pair);
+      run_fin(fp);
     } else {
-      stream_blocks<kRing, Tile>(first, step, n_full, load_tile,
-                                 [&](int j, const Tile& t) { process(std::false_type{}, j, t); });
-      if (tail_masked && n_full % step == first) {
-        Tile t;
-        load_tile(n_full, t);
-        process(std::true_type{}, n_full, t);
+      stream_blocks<kRing, Pair>(0, 1, pairs, load_pair, proc_pair);
+      if (fin) {
+        Pair fp;
+        load_tile(j_fin, fp.a);
+        if (fin == 2) load_tile(j_fin + step, fp.b);
+        run_fin(fp);
       }
     }
   };
