@@ -14,16 +14,18 @@
 //    token * G + head within the group, so grouped heads share every K/V
 //    tile), split into 16-row tiles over the waves (one tile per wave was
 //    measured faster than two: the cost per block is not the LDS reads);
-//  * the workgroup streams the sequence's 16-token blocks up to the last
-//    position among its rows. Each block's K and V tile is loaded once, by all
-//    four waves together, into double-buffered LDS (rows padded by 16 bytes
-//    against bank conflicts; FP8 widened exactly to the 16-bit type), while
-//    the waves compute on the previous block;
-//  * per wave and block, S = K·Qᵀ is 16x16x32 MFMAs on K read from LDS in the
+//  * the workgroup streams the sequence's 16-token blocks, two per step, up
+//    to the last position among its rows. Each block's K and V tile is loaded
+//    once, by all four waves together, into double-buffered LDS (rows padded
+//    by 16 bytes against bank conflicts; FP8 widened exactly to the 16-bit
+//    type), while the waves compute on the previous step;
+//  * per wave and step, S = K·Qᵀ is 16x16x32 MFMAs on K read from LDS in the
 //    A-operand layout; the lane layout of S is the A-operand layout of P, so
 //    the online softmax (a lazily moved per-row reference max) runs in place;
-//    O += P·V is 16x16x16 MFMAs with P split into 16-bit hi + lo and V read
-//    transposed from LDS;
+//    O += P·V is one 16x16x32 MFMA per 16 output columns and P part (P split
+//    into 16-bit hi + lo), its 32 keys being this lane group's four rows of
+//    each of the two blocks, matched by two transposed reads of V from LDS
+//    (on gfx950 the 16x16x32 form issues in the same time as 16x16x16);
 //  * causality is a per-row limit on the key index, applied by selection; a
 //    wave whose rows all end before a block skips its arithmetic.
 // No split over keys is done: a chunk's rows already give many workgroups.
@@ -34,6 +36,8 @@ namespace pa {
 namespace {
 
 constexpr int kRT = kPrefillRows / (16 * kWaves);  // 16-row tiles per wave
+constexpr int kSB = 2;                              // blocks per step (the P·V operands below pair two)
+static_assert(kSB == 2, "one 16x16x32 P·V product spans two blocks");
 constexpr float kPSlack = 8.0f;
 static_assert(kRT * 16 * kWaves == kPrefillRows, "rows split evenly over the waves");
 
@@ -54,8 +58,8 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma(const PrefillArgs a) {
   constexpr int NL = G::NL, NLW = G::NLW, NKB = G::NKB, NDB = G::NDB, S = G::S;
   static_assert(QK == kF16 || QK == kBF16, "16-bit queries");
 
-  __shared__ __align__(16) uint16_t s_k[2][16 * S];
-  __shared__ __align__(16) uint16_t s_v[2][16 * S];
+  __shared__ __align__(16) uint16_t s_k[2][kSB][16 * S];
+  __shared__ __align__(16) uint16_t s_v[2][kSB][16 * S];
 
   const int kvh = blockIdx.x / a.row_tiles;
   const int rt = blockIdx.x - kvh * a.row_tiles;
@@ -106,46 +110,60 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma(const PrefillArgs a) {
   const char* kbase = static_cast<const char*>(a.k_cache) + (int64_t)kvh * G::kTileBytes;
   const char* vbase = static_cast<const char*>(a.v_cache) + (int64_t)kvh * G::kTileBytes;
 
-  // Block j's tiles, as this wave's share of the 2*NL wave-loads (K first, then V).
-  uint4 pre[NLW];
+  // The tiles of step j (blocks kSB*j .. kSB*j + kSB - 1), as this wave's
+  // share of the 2*NL wave-loads per block (K first, then V). A block past
+  // the last one needed is not loaded (its table entry may lie past the row):
+  // its keys are beyond every row's limit, and it is staged as zeros.
+  uint4 pre[kSB][NLW];
   auto issue = [&](int j) {
-    const int phys = __builtin_amdgcn_readfirstlane(bt[j]);
-    const int64_t off = ((uint32_t)phys < (uint64_t)a.num_blocks ? phys : 0) * blk_stride;
 #pragma unroll
-    for (int u = 0; u < NLW; ++u) {
-      const int L = wave + u * kWaves;
-      if (L < 2 * NL) {
-        const char* base = L < NL ? kbase : vbase;
-        pre[u] = load_stream(base + off + (L % NL) * 1024 + lane * 16);
+    for (int p = 0; p < kSB; ++p) {
+      const int blk = kSB * j + p;
+      if (blk >= nblk) continue;
+      const int phys = __builtin_amdgcn_readfirstlane(bt[blk]);
+      const int64_t off = ((uint32_t)phys < (uint64_t)a.num_blocks ? phys : 0) * blk_stride;
+#pragma unroll
+      for (int u = 0; u < NLW; ++u) {
+        const int L = wave + u * kWaves;
+        if (L < 2 * NL) {
+          const char* base = L < NL ? kbase : vbase;
+          pre[p][u] = load_stream(base + off + (L % NL) * 1024 + lane * 16);
+        }
       }
     }
   };
   auto stage = [&](int j, int buf) {
 #pragma unroll
-    for (int u = 0; u < NLW; ++u) {
-      const int L = wave + u * kWaves;
-      if (L < 2 * NL) {
-        const bool is_v = L >= NL;
-        const int byte = (L % NL) * 1024 + lane * 16;
-        const int row = byte / G::kRowBytes;
-        const int col = (byte % G::kRowBytes) / G::kBytes;
-        // rows past the context may hold anything: V rows there become zero
-        // (a zero weight times NaN would still be NaN); K rows are masked later
-        const bool zero = is_v && j * 16 + row >= ctx;
-        uint16_t* dst = (is_v ? s_v[buf] : s_k[buf]) + row * S + col;
-        uint4 v = pre[u];
-        if constexpr (CK == kFP8) {
-          uint4 w0, w1;
-          fp8x4_to_16<QK>(v.x, w0.x, w0.y);
-          fp8x4_to_16<QK>(v.y, w0.z, w0.w);
-          fp8x4_to_16<QK>(v.z, w1.x, w1.y);
-          fp8x4_to_16<QK>(v.w, w1.z, w1.w);
-          if (zero) w0 = w1 = make_uint4(0u, 0u, 0u, 0u);
-          *reinterpret_cast<uint4*>(dst) = w0;
-          *reinterpret_cast<uint4*>(dst + 8) = w1;
-        } else {
-          if (zero) v = make_uint4(0u, 0u, 0u, 0u);
-          *reinterpret_cast<uint4*>(dst) = v;
+    for (int p = 0; p < kSB; ++p) {
+      const int blk = kSB * j + p;
+#pragma unroll
+      for (int u = 0; u < NLW; ++u) {
+        const int L = wave + u * kWaves;
+        if (L < 2 * NL) {
+          const bool is_v = L >= NL;
+          const int byte = (L % NL) * 1024 + lane * 16;
+          const int row = byte / G::kRowBytes;
+          const int col = (byte % G::kRowBytes) / G::kBytes;
+          // rows past the context may hold anything: V rows there become zero
+          // (a zero weight times NaN would still be NaN); K rows are masked
+          // later; a block not loaded is zero throughout
+          const bool absent = blk >= nblk;
+          const bool zero = absent || (is_v && blk * 16 + row >= ctx);
+          uint16_t* dst = (is_v ? s_v[buf][p] : s_k[buf][p]) + row * S + col;
+          uint4 v = absent ? make_uint4(0u, 0u, 0u, 0u) : pre[p][u];
+          if constexpr (CK == kFP8) {
+            uint4 w0, w1;
+            fp8x4_to_16<QK>(v.x, w0.x, w0.y);
+            fp8x4_to_16<QK>(v.y, w0.z, w0.w);
+            fp8x4_to_16<QK>(v.z, w1.x, w1.y);
+            fp8x4_to_16<QK>(v.w, w1.z, w1.w);
+            if (zero) w0 = w1 = make_uint4(0u, 0u, 0u, 0u);
+            *reinterpret_cast<uint4*>(dst) = w0;
+            *reinterpret_cast<uint4*>(dst + 8) = w1;
+          } else {
+            if (zero) v = make_uint4(0u, 0u, 0u, 0u);
+            *reinterpret_cast<uint4*>(dst) = v;
+          }
         }
       }
     }
@@ -165,29 +183,38 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma(const PrefillArgs a) {
   const float qk_scale = a.qk_scale;
 
   auto compute = [&](int j, int buf) {
-    if (j * 16 >= wave_limit) return;  // every row of this wave ends before this block
-    const uint16_t* sk = s_k[buf];
-    const uint16_t* sv = s_v[buf];
-    f32x4_t s[kRT];
+    const int key0 = kSB * 16 * j;  // first key of the step
+    if (key0 >= wave_limit) return;  // every row of this wave ends before this step
+    f32x4_t s[kRT][kSB];
 #pragma unroll
-    for (int t = 0; t < kRT; ++t) s[t] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < kRT; ++t)
 #pragma unroll
-    for (int b = 0; b < NKB; ++b) {
-      const uint4 kw = *reinterpret_cast<const uint4*>(sk + n * S + 32 * b + 8 * g);
-      const uint32_t w[4] = {kw.x, kw.y, kw.z, kw.w};
+      for (int p = 0; p < kSB; ++p) s[t][p] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int t = 0; t < kRT; ++t) s[t] = mma_k32<QK>(w, qf[t][b], s[t]);
+    for (int p = 0; p < kSB; ++p) {
+      const uint16_t* sk = s_k[buf][p];
+#pragma unroll
+      for (int b = 0; b < NKB; ++b) {
+        const uint4 kw = *reinterpret_cast<const uint4*>(sk + n * S + 32 * b + 8 * g);
+        const uint32_t w[4] = {kw.x, kw.y, kw.z, kw.w};
+#pragma unroll
+        for (int t = 0; t < kRT; ++t) s[t][p] = mma_k32<QK>(w, qf[t][b], s[t][p]);
+      }
     }
-    uint32_t ph[kRT][2], pl[kRT][2];
+    uint32_t ph[kRT][kSB][2], pl[kRT][kSB][2];
 #pragma unroll
     for (int t = 0; t < kRT; ++t) {
-      float x[4];
+      float x[kSB][4];
+      float bm = kNegInf;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[i] = s[t][i] * qk_scale;
-        if (j * 16 + 4 * g + i >= my_limit[t]) x[i] = kNegInf;  // causal limit (and rows past the chunk)
-      }
-      const float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      for (int p = 0; p < kSB; ++p)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[p][i] = s[t][p][i] * qk_scale;
+          // causal limit (and rows past the chunk), by selection
+          if (key0 + 16 * p + 4 * g + i >= my_limit[t]) x[p][i] = kNegInf;
+          bm = fmaxf(bm, x[p][i]);
+        }
       if (__builtin_amdgcn_ballot_w64(bm > mref[t] + kPSlack) != 0) {
         float bmx = fmaxf(bm, __shfl_xor(bm, 16, 64));
         bmx = fmaxf(bmx, __shfl_xor(bmx, 32, 64));
@@ -203,33 +230,41 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma(const PrefillArgs a) {
         }
       }
       const float ms = (mref[t] == kNegInf) ? 0.f : mref[t];
-      float p[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[i] = fast_exp2(x[i] - ms);
-        lsum[t] += p[i];
+      for (int p = 0; p < kSB; ++p) {
+        float pr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pr[i] = fast_exp2(x[p][i] - ms);
+          lsum[t] += pr[i];
+        }
+        ph[t][p][0] = pack2<QK>(pr[0], pr[1]);
+        ph[t][p][1] = pack2<QK>(pr[2], pr[3]);
+        pl[t][p][0] = pack2<QK>(pr[0] - lo16_to_f32<QK>(ph[t][p][0]), pr[1] - hi16_to_f32<QK>(ph[t][p][0]));
+        pl[t][p][1] = pack2<QK>(pr[2] - lo16_to_f32<QK>(ph[t][p][1]), pr[3] - hi16_to_f32<QK>(ph[t][p][1]));
       }
-      ph[t][0] = pack2<QK>(p[0], p[1]);
-      ph[t][1] = pack2<QK>(p[2], p[3]);
-      pl[t][0] = pack2<QK>(p[0] - lo16_to_f32<QK>(ph[t][0]), p[1] - hi16_to_f32<QK>(ph[t][0]));
-      pl[t][1] = pack2<QK>(p[2] - lo16_to_f32<QK>(ph[t][1]), p[3] - hi16_to_f32<QK>(ph[t][1]));
     }
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const u32x2_t b = v_operand_tr(sv, S, db * 16, lane);
+      const u32x2_t b0 = v_operand_tr(s_v[buf][0], S, db * 16, lane);
+      const u32x2_t b1 = v_operand_tr(s_v[buf][1], S, db * 16, lane);
+      const uint32_t b[4] = {b0[0], b0[1], b1[0], b1[1]};
 #pragma unroll
       for (int t = 0; t < kRT; ++t) {
-        acc[t][db] = mma_k16<QK>(ph[t][0], ph[t][1], b[0], b[1], acc[t][db]);
-        acc[t][db] = mma_k16<QK>(pl[t][0], pl[t][1], b[0], b[1], acc[t][db]);
+        const uint32_t ah[4] = {ph[t][0][0], ph[t][0][1], ph[t][1][0], ph[t][1][1]};
+        const uint32_t al[4] = {pl[t][0][0], pl[t][0][1], pl[t][1][0], pl[t][1][1]};
+        acc[t][db] = mma_k32<QK>(ah, b, acc[t][db]);
+        acc[t][db] = mma_k32<QK>(al, b, acc[t][db]);
       }
     }
   };
 
+  const int nsteps = (nblk + kSB - 1) / kSB;
   issue(0);
   stage(0, 0);
   __syncthreads();
-  for (int j = 0; j < nblk; ++j) {
-    const bool more = j + 1 < nblk;
+  for (int j = 0; j < nsteps; ++j) {
+    const bool more = j + 1 < nsteps;
     if (more) issue(j + 1);
     __builtin_amdgcn_sched_barrier(0);
     compute(j, j & 1);
