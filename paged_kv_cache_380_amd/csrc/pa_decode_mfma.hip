@@ -26,7 +26,7 @@
 //    which is exactly the A-operand layout of P in O += P·V: the softmax runs
 //    in place, per lane, with no shuffle of P.
 //  * V must be read token-major per lane, so each wave stages its V tile in
-//    LDS (rows padded by 16 bytes against bank conflicts; FP8 widened to the
+//    LDS (rows padded by 32 bytes against bank conflicts; FP8 widened to the
 //    16-bit type on the way) and reads the B operand back transposed, one
 //    ds_read_b64_tr_b16 per 16 columns.
 //  * P is rounded to the 16-bit type as hi + lo (two MFMAs per D-slice), so the
@@ -68,7 +68,10 @@ template <int CK, int D> struct MGeo {
   static constexpr int NKL = (CK == kFP8) ? D / 64 : D / 32;  // K loads per lane (16 bytes each)
   static constexpr int NVL = kTileBytes / 1024;           // V loads per lane (16 bytes each)
   static constexpr int NDB = D / 16;                      // 16-wide column blocks of O
-  static constexpr int kVStride = D + 8;                  // LDS row stride of the staged V tile (16-bit elements)
+  // LDS row stride of the staged V tile (16-bit elements). V is read back
+  // transposed, 8 bytes per lane from 4 rows x 4 column pairs: a stride of
+  // 8 or 40 (mod 64) dwords puts the 32 lanes of a pass on distinct banks.
+  static constexpr int kVStride = D + 16;
   static_assert(NVL >= 1, "tile smaller than one wave-load");
 };
 

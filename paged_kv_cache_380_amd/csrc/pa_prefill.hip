@@ -49,17 +49,23 @@ template <int CK, int D> struct PGeo {
   static constexpr int NLW = (2 * NL + kWaves - 1) / kWaves;  // loads per wave per block (K and V together)
   static constexpr int NKB = D / 32;
   static constexpr int NDB = D / 16;
-  static constexpr int S = D + 8;                    // LDS row stride of a staged tile, 16-bit elements
+  // LDS row strides of the staged tiles, 16-bit elements. K rows are read
+  // 16 bytes per lane down 16 rows: a stride of 4 (mod 16) dwords puts the
+  // 16 lanes of a pass on distinct banks. V is read back transposed, 8 bytes
+  // per lane from 4 rows x 4 column pairs: a stride of 8 or 40 (mod 64) dwords
+  // keeps the 32 lanes of a pass on distinct banks.
+  static constexpr int S = D + 8;    // K
+  static constexpr int SV = D + 16;  // V
 };
 
 template <int QK, int CK, int D>
 __global__ __launch_bounds__(kThreads) void prefill_mfma(const PrefillArgs a) {
   using G = PGeo<CK, D>;
-  constexpr int NL = G::NL, NLW = G::NLW, NKB = G::NKB, NDB = G::NDB, S = G::S;
+  constexpr int NL = G::NL, NLW = G::NLW, NKB = G::NKB, NDB = G::NDB, S = G::S, SV = G::SV;
   static_assert(QK == kF16 || QK == kBF16, "16-bit queries");
 
   __shared__ __align__(16) uint16_t s_k[2][kSB][16 * S];
-  __shared__ __align__(16) uint16_t s_v[2][kSB][16 * S];
+  __shared__ __align__(16) uint16_t s_v[2][kSB][16 * SV];
 
   const int kvh = blockIdx.x / a.row_tiles;
   const int rt = blockIdx.x - kvh * a.row_tiles;
@@ -111,34 +117,38 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma(const PrefillArgs a) {
   const char* vbase = static_cast<const char*>(a.v_cache) + (int64_t)kvh * G::kTileBytes;
 
   // The tiles of step j (blocks kSB*j .. kSB*j + kSB - 1), as this wave's
-  // share of the 2*NL wave-loads per block (K first, then V). A block past
-  // the last one needed is not loaded (its table entry may lie past the row):
-  // its keys are beyond every row's limit, and it is staged as zeros.
-  uint4 pre[kSB][NLW];
-  auto issue = [&](int j) {
+  // share of the 2*NL wave-loads per block (K first, then V), into register
+  // buffer rb; loads run two steps ahead of the arithmetic. The loads are
+  // unconditional, so that the compiler's wait before staging a step counts
+  // the newer step's loads and leaves them in flight: a block past the last
+  // one needed (its table entry may lie past the row) reloads the last
+  // block, and is staged as zeros (its keys are beyond every row's limit).
+  uint4 pre[2][kSB][NLW];
+  auto issue = [&](int j, int rb) {
 #pragma unroll
     for (int p = 0; p < kSB; ++p) {
-      const int blk = kSB * j + p;
-      if (blk >= nblk) continue;
-      const int phys = __builtin_amdgcn_readfirstlane(bt[blk]);
+      const int blk = min(kSB * j + p, nblk - 1);
+      // A scalar load (the table is read-only here): waiting for it does not
+      // wait for the vector loads of the steps in flight.
+      const int phys = ((const __attribute__((address_space(4))) int32_t*)bt)[blk];
       const int64_t off = ((uint32_t)phys < (uint64_t)a.num_blocks ? phys : 0) * blk_stride;
 #pragma unroll
       for (int u = 0; u < NLW; ++u) {
-        const int L = wave + u * kWaves;
+        const int L = (wave & (kWaves - 1)) + u * kWaves;  // wave < kWaves, stated for the compiler
         if (L < 2 * NL) {
           const char* base = L < NL ? kbase : vbase;
-          pre[p][u] = load_stream(base + off + (L % NL) * 1024 + lane * 16);
+          pre[rb][p][u] = load_stream(base + off + (L % NL) * 1024 + lane * 16);
         }
       }
     }
   };
-  auto stage = [&](int j, int buf) {
+  auto stage = [&](int j, int buf, int rb) {
 #pragma unroll
     for (int p = 0; p < kSB; ++p) {
       const int blk = kSB * j + p;
 #pragma unroll
       for (int u = 0; u < NLW; ++u) {
-        const int L = wave + u * kWaves;
+        const int L = (wave & (kWaves - 1)) + u * kWaves;  // wave < kWaves, stated for the compiler
         if (L < 2 * NL) {
           const bool is_v = L >= NL;
           const int byte = (L % NL) * 1024 + lane * 16;
@@ -149,8 +159,8 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma(const PrefillArgs a) {
           // later; a block not loaded is zero throughout
           const bool absent = blk >= nblk;
           const bool zero = absent || (is_v && blk * 16 + row >= ctx);
-          uint16_t* dst = (is_v ? s_v[buf][p] : s_k[buf][p]) + row * S + col;
-          uint4 v = absent ? make_uint4(0u, 0u, 0u, 0u) : pre[p][u];
+          uint16_t* dst = is_v ? s_v[buf][p] + row * SV + col : s_k[buf][p] + row * S + col;
+          uint4 v = absent ? make_uint4(0u, 0u, 0u, 0u) : pre[rb][p][u];
           if constexpr (CK == kFP8) {
             uint4 w0, w1;
             fp8x4_to_16<QK>(v.x, w0.x, w0.y);
@@ -246,8 +256,8 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma(const PrefillArgs a) {
     }
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const u32x2_t b0 = v_operand_tr(s_v[buf][0], S, db * 16, lane);
-      const u32x2_t b1 = v_operand_tr(s_v[buf][1], S, db * 16, lane);
+      const u32x2_t b0 = v_operand_tr(s_v[buf][0], SV, db * 16, lane);
+      const u32x2_t b1 = v_operand_tr(s_v[buf][1], SV, db * 16, lane);
       const uint32_t b[4] = {b0[0], b0[1], b1[0], b1[1]};
 #pragma unroll
       for (int t = 0; t < kRT; ++t) {
@@ -260,16 +270,26 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma(const PrefillArgs a) {
   };
 
   const int nsteps = (nblk + kSB - 1) / kSB;
-  issue(0);
-  stage(0, 0);
+  issue(0, 0);
+  issue(1, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  stage(0, 0, 0);
   __syncthreads();
-  for (int j = 0; j < nsteps; ++j) {
-    const bool more = j + 1 < nsteps;
-    if (more) issue(j + 1);
+  // Two steps per iteration, so that both register buffers have fixed names
+  // (an indexed choice between them made the compiler wait for every load).
+  for (int j = 0; j < nsteps; j += 2) {
+    issue(j + 2, 0);  // step j's registers were staged last iteration
     __builtin_amdgcn_sched_barrier(0);
-    compute(j, j & 1);
+    compute(j, 0);
     __builtin_amdgcn_sched_barrier(0);
-    if (more) stage(j + 1, (j + 1) & 1);
+    stage(j + 1, 1, 1);  // past the last step: zeros, unused
+    __syncthreads();
+    if (j + 1 >= nsteps) break;
+    issue(j + 3, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(j + 1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    stage(j + 2, 0, 0);
     __syncthreads();
   }
 
