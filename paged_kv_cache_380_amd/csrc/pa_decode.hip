@@ -682,7 +682,7 @@ __global__ __launch_bounds__(64) void decode_bal_reduce(const DecodeArgs a) {
     // Common case, one round of loads: lane i takes piece i's max and sum,
     // every lane its columns of the first kPre pieces' outputs; the weights
     // are then shared by lane reads.
-    constexpr int kPre = 8;
+    constexpr int kPre = 16;
     float ov[kPre][D / 64];
 #pragma unroll
     for (int j = 0; j < kPre; ++j)
