@@ -146,6 +146,12 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma(const PrefillArgs a) {
 #pragma unroll
     for (int p = 0; p < kSB; ++p) {
       const int blk = kSB * j + p;
+      // Blocks before the last needed one lie wholly inside the context and
+      // are stored as loaded; the last one (rows past the context may hold
+      // anything: V rows there become zero, as a zero weight times NaN would
+      // still be NaN; K rows are masked later) and blocks not needed (zero
+      // throughout) go through selection.
+      const bool inside = blk + 1 < nblk;
 #pragma unroll
       for (int u = 0; u < NLW; ++u) {
         const int L = (wave & (kWaves - 1)) + u * kWaves;  // wave < kWaves, stated for the compiler
@@ -154,24 +160,21 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma(const PrefillArgs a) {
           const int byte = (L % NL) * 1024 + lane * 16;
           const int row = byte / G::kRowBytes;
           const int col = (byte % G::kRowBytes) / G::kBytes;
-          // rows past the context may hold anything: V rows there become zero
-          // (a zero weight times NaN would still be NaN); K rows are masked
-          // later; a block not loaded is zero throughout
-          const bool absent = blk >= nblk;
-          const bool zero = absent || (is_v && blk * 16 + row >= ctx);
           uint16_t* dst = is_v ? s_v[buf][p] + row * SV + col : s_k[buf][p] + row * S + col;
-          uint4 v = absent ? make_uint4(0u, 0u, 0u, 0u) : pre[rb][p][u];
+          uint4 v = pre[rb][p][u];
+          if (!inside) {
+            const bool zero = blk >= nblk || (is_v && blk * 16 + row >= ctx);
+            if (zero) v = make_uint4(0u, 0u, 0u, 0u);
+          }
           if constexpr (CK == kFP8) {
             uint4 w0, w1;
             fp8x4_to_16<QK>(v.x, w0.x, w0.y);
             fp8x4_to_16<QK>(v.y, w0.z, w0.w);
             fp8x4_to_16<QK>(v.z, w1.x, w1.y);
             fp8x4_to_16<QK>(v.w, w1.z, w1.w);
-            if (zero) w0 = w1 = make_uint4(0u, 0u, 0u, 0u);
             *reinterpret_cast<uint4*>(dst) = w0;
             *reinterpret_cast<uint4*>(dst + 8) = w1;
           } else {
-            if (zero) v = make_uint4(0u, 0u, 0u, 0u);
             *reinterpret_cast<uint4*>(dst) = v;
           }
         }
