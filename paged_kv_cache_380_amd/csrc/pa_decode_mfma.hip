@@ -10,40 +10,53 @@
 // [16 tokens × D]·[D × GT heads] and O += P·V is [GT × 16]·[16 × D]. On the
 // vector ALU these products cost about 600 instructions per tile at GT = 8,
 // which leaves the kernel ALU-bound below the HBM roofline; here they are
-// issued as MFMA instructions (16×16×32 for S, 16×16×16 for O), and the
-// vector ALU only runs the online softmax.
+// issued as MFMA instructions, and the vector ALU only runs the online softmax.
 //
-//  * One workgroup of 4 waves per (sequence, KV head, head tile of GT <= 16,
-//    partition), wave w taking blocks w, w+4, ... of the partition, exactly as
-//    the vector kernels do, with the block-table slice staged in LDS and the
-//    next block's K/V loads in flight while the current one is used.
+// Two schedules share the per-block arithmetic below:
+//  * partitioned: one workgroup of 4 waves per (sequence, KV head, head tile
+//    of GT <= 16, partition), wave w taking blocks w, w+4, ... of the
+//    partition, with the block-table slice staged in LDS; the waves merge
+//    through LDS at the end;
+//  * balanced (kBalanced): the blocks of all sequences are laid end to end
+//    and cut into equal ranges, one per wave, whatever the context lengths;
+//    each wave streams its range piece by piece (a piece is the part of one
+//    sequence inside the range) and leaves each piece's partial result for
+//    decode_bal_reduce, or writes a sequence it holds whole. GT may be 32
+//    here: two 16-head sub-tiles per wave share every K/V block it loads.
+// In both, a wave keeps the next blocks' K/V loads in flight while it works.
+//
 //  * K is loaded straight from HBM in the MFMA A-operand layout: lane l reads
 //    16 bytes of token l % 16 (64 contiguous bytes per token per instruction),
 //    so S needs no data movement at all. The head dimension may be taken in
 //    any order as long as q is read in the same order (a dot product does not
-//    care), which lets FP8 rows be read 16 bytes at a time.
+//    care), which lets FP8 rows be read 16 bytes at a time. S is 16×16×32
+//    MFMAs.
 //  * S comes out with lane l holding head l % 16 for tokens 4·(l/16) + i,
 //    which is exactly the A-operand layout of P in O += P·V: the softmax runs
 //    in place, per lane, with no shuffle of P.
-//  * V must be read token-major per lane, so each wave stages its V tile in
+//  * V must be read token-major per lane, so each wave stages its V tiles in
 //    LDS (rows padded by 32 bytes against bank conflicts; FP8 widened to the
 //    16-bit type on the way) and reads the B operand back transposed, one
-//    ds_read_b64_tr_b16 per 16 columns.
+//    ds_read_b64_tr_b16 per 16 columns and block.
+//  * Blocks go two per step: O += P·V for the pair is one 16×16×32 MFMA per 16
+//    columns (its 32 tokens are this lane group's four rows of each block),
+//    which issues in the time of one 16×16×16 MFMA. A leftover block and the
+//    masked tail block form a peeled last step (16×16×16 for a single block).
 //  * P is rounded to the 16-bit type as hi + lo (two MFMAs per D-slice), so the
 //    weights keep about 16 significant bits and the output stays within float32
 //    accumulation error of the exact weights; V, K and q are exact in the
 //    16-bit type (FP8 codes widen exactly).
-//  * When a KV head has several head tiles (more than 16 query heads per KV
-//    head), their workgroups read the same K/V. Then K/V are loaded with the
-//    ordinary (cached) hint and the workgroups are renumbered so that the
-//    tiles of one (sequence, KV head, partition) get consecutive numbers on the
-//    same XCD: the hardware hands workgroups to the 8 XCDs in turn, so dispatch
-//    index i runs on XCD i mod 8, and the tiles that share data then run side
-//    by side behind one L2. With a single tile per KV head nothing is reused
-//    and the loads stay streaming (nontemporal), in launch order.
-//  * The running max is moved lazily: only when a tile's max exceeds it by more
-//    than kSlack (log2 units) is it raised and the accumulators rescaled; all
-//    weights stay below 2^kSlack, which float32 sums hold easily.
+//  * When a KV head has several head tiles (more query heads per KV head than
+//    one wave takes), their workgroups read the same K/V. Then K/V are loaded
+//    with the ordinary (cached) hint and the workgroups are renumbered so that
+//    the tiles of one (sequence or range, KV head) get consecutive numbers on
+//    the same XCD: the hardware hands workgroups to the 8 XCDs in turn, so
+//    dispatch index i runs on XCD i mod 8, and the tiles that share data then
+//    run side by side behind one L2. With a single tile per KV head nothing is
+//    reused and the loads stay streaming (nontemporal), in launch order.
+//  * The running max is moved lazily: only when a step's max exceeds it by
+//    more than kSlack (log2 units) is it raised and the accumulators rescaled;
+//    all weights stay below 2^kSlack, which float32 sums hold easily.
 // Rows past the context get a -inf logit by selection and a zero V row, so
 // stale or NaN data there never reaches the output.
 #include <type_traits>
