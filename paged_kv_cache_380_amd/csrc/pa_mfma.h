@@ -78,9 +78,10 @@ __device__ __forceinline__ void fp8x4_to_16(uint32_t w, uint32_t& lo, uint32_t& 
   }
 }
 
-// The B operand of a 16x16x16 product O += P·V from a row-major V tile in
-// LDS (16 rows of `stride` 16-bit elements): lane l gets V[4(l/16) + e][c0 +
-// l % 16] for e = 0..3, i.e. four tokens of one column, as two packed words.
+// The B operand of a 16x16x16 product O += P·V (or half of a 16x16x32 one
+// over two tiles) from a row-major V tile in LDS (16 rows of `stride` 16-bit
+// elements): lane l gets V[4(l/16) + e][c0 + l % 16] for e = 0..3, i.e. four
+// tokens of one column, as two packed words.
 // One transposing LDS read (ds_read_b64_tr_b16) does it: within each 16-lane
 // group, output lane i element e comes from lane 4e + i/4, element i % 4, so
 // lane l supplies the 8 bytes at row 4(l/16) + (l%16)/4, column
