@@ -88,8 +88,8 @@ struct PrefillArgs {
   int out_kind;
 };
 
-// Rows ((token, head) pairs of one KV head) per prefill workgroup.
-constexpr int kPrefillRows = 64;
+// Rows ((token, head) pairs of one KV head) per prefill workgroup (16 per wave).
+constexpr int kPrefillRows = 128;
 
 hipError_t launch_prefill(const PrefillArgs& a, int q_kind, int cache_kind, hipStream_t stream);
 
