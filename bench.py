@@ -217,6 +217,9 @@ def main():
                     metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR", "COPY_MIB", "OUT"),
                     help="write the HBM-traffic summary of rocprofv3 --pmc runs for --workload and exit")
     ap.add_argument("--command", action="append", default=[], help="profiling commands recorded in a summary")
+    ap.add_argument("--shared-prefix", choices=("auto", "on", "off"), default="auto",
+                    help="decode through pa_decode_shared_prefix with the workload's prefix group (auto: when "
+                         "its sequences share a prefix and the grouped reading applies)")
     ap.add_argument("--op", choices=("decode", "prefill", "copy"), default="decode",
                     help="decode: the decode step (default, the headline); prefill: chunked-prefill attention "
                          "(TFLOP/s); copy: copy-on-write block copies (GB/s)")
@@ -266,15 +269,32 @@ def main():
     w = wl.named(args.workload, args.seed)
     case = GpuCase(w, device=dev)
     out = torch.empty(case.q.shape, dtype=case.q.dtype, device=dev)
-    ws = binding.workspace_for(case.q, w.num_kv_heads, case.tables, args.partition_blocks)
     pb = args.partition_blocks or binding.decode_partition_blocks(w.num_seqs, w.num_heads, w.num_kv_heads,
                                                                   w.head_size, w.max_blocks_per_seq)
     stream = torch.cuda.current_stream(dev)
+    prefix = shared_prefix_applies(w, args.partition_blocks) if args.shared_prefix == "auto" else \
+        args.shared_prefix == "on"
+    if prefix:
+        if not w.sharing_seqs:
+            raise SystemExit(f"--shared-prefix on: {w.name} has no shared prefix")
+        groups = [(0, w.sharing_seqs, w.shared_blocks)]
+        nbytes = binding.shared_prefix_workspace_bytes(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_size,
+                                                       w.max_blocks_per_seq, w.shared_blocks)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev) if nbytes else None
+
+        def run_decode():
+            binding.decode_shared_prefix(out, case.q, case.kc, case.vc, case.tables, case.lens, w.scale,
+                                         w.num_kv_heads, groups, w.block_size, w.k_scale, w.v_scale, workspace=ws)
+    else:
+        ws = binding.workspace_for(case.q, w.num_kv_heads, case.tables, args.partition_blocks)
+
+        def run_decode():
+            binding.decode(out, case.q, case.kc, case.vc, case.tables, case.lens, w.scale, w.num_kv_heads,
+                           w.block_size, w.k_scale, w.v_scale, partition_blocks=args.partition_blocks, workspace=ws)
 
     def step():
         case.append()
-        binding.decode(out, case.q, case.kc, case.vc, case.tables, case.lens, w.scale, w.num_kv_heads,
-                       w.block_size, w.k_scale, w.v_scale, partition_blocks=args.partition_blocks, workspace=ws)
+        run_decode()
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -296,8 +316,7 @@ def main():
     for a, b in ev:
         case.append()
         a.record(stream)
-        binding.decode(out, case.q, case.kc, case.vc, case.tables, case.lens, w.scale, w.num_kv_heads,
-                       w.block_size, w.k_scale, w.v_scale, partition_blocks=args.partition_blocks, workspace=ws)
+        run_decode()
         b.record(stream)
     torch.cuda.synchronize()
     durs = sorted(a.elapsed_time(b) for a, b in ev)
@@ -330,13 +349,14 @@ def main():
             "kv_cache_dtype": w.cache_dtype, "seed": w.seed,
             "schedule": "balanced" if balanced_schedule(w, args.partition_blocks) else f"partitions of {pb} blocks",
             "decode_path": os.environ.get("PA_DECODE_PATH", "auto"),
+            "shared_prefix": [0, w.sharing_seqs, w.shared_blocks] if prefix else None,
         },
         "pct_of_hbm_peak": round(100 * kv_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
         "seq_steps_per_s": round(w.num_seqs / (ms_per_step * 1e-3), 1),
         "decode_ms": round(decode_ms, 5),
         "decode_ms_p10_p90": [round(durs[len(durs) // 10], 5), round(durs[(9 * len(durs)) // 10], 5)],
         "roofline": {
-            "kernel": decode_kernels(w, args.partition_blocks, pb),
+            "kernel": ("decode_mfma[shared prefix] + " if prefix else "") + decode_kernels(w, args.partition_blocks, pb),
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": None if traffic is None else round(traffic),
@@ -461,6 +481,12 @@ def balanced_schedule(w, partition_blocks: int) -> bool:
     """Whether the library picks its balanced schedule here (its selection rule, restated)."""
     return (decode_kernel(w) == "decode_mfma" and partition_blocks == 0 and w.num_seqs <= 1024
             and w.num_seqs * w.max_blocks_per_seq <= 2**31 - 1)
+
+
+def shared_prefix_applies(w, partition_blocks: int) -> bool:
+    """Whether the shared-prefix pass runs for this workload's prefix group (the library's rule, restated)."""
+    group = w.num_heads // w.num_kv_heads
+    return bool(w.sharing_seqs) and balanced_schedule(w, partition_blocks) and group >= 4 and 16 % group == 0
 
 
 def decode_kernels(w, partition_blocks: int, pb: int) -> str:

@@ -30,8 +30,9 @@
  *
  * Query head h reads KV head h / (num_heads / num_kv_heads).
  *
- * Ownership: every pointer is device memory owned by the caller and must stay
- * valid until the work queued on `stream` has finished. The library never
+ * Ownership: every pointer is device memory owned by the caller (except those
+ * documented as host arrays, read during the call) and must stay valid until
+ * the work queued on `stream` has finished. The library never
  * allocates, frees, copies to the host or synchronises; both calls only queue
  * kernels on `stream` (a hipStream_t; NULL is the default stream) and return.
  * They hold no global state besides a thread-local error message and are safe
@@ -219,6 +220,51 @@ int pa_decode_split(void* out, const void* q, const void* k_cache, const void* v
  */
 size_t pa_decode_workspace_bytes(int num_seqs, int num_heads, int num_kv_heads, int head_size,
                                  int max_blocks_per_seq, int block_size, int partition_blocks);
+
+/*
+ * pa_decode_shared_prefix -- pa_decode for a batch in which groups of
+ * sequences share the first physical blocks of their block tables ("vLLM
+ * 前世今生" §3.2: sequences that share a prompt prefix map it to the same
+ * physical blocks; "vLLM" note, section "前缀缓存": prefix caching). The
+ * result is pa_decode's (up to float32 rounding order); only the reading of
+ * the shared blocks changes: they are read once per 16 / G sequences of a
+ * group (G = num_heads / num_kv_heads) instead of once per sequence.
+ *
+ *   prefix_groups  host, int32 [num_groups][3]: (first_seq, num_seqs, shared_blocks).
+ *                  Group i is sequences first_seq .. first_seq + num_seqs - 1,
+ *                  whose block-table entries 0 .. shared_blocks - 1 are equal
+ *                  (the first sequence's row is the one read) and whose contexts
+ *                  hold at least shared_blocks * block_size tokens. Groups are
+ *                  ordered and disjoint; 1 <= shared_blocks <= max_blocks_per_seq.
+ *                  Read during the call only.
+ *   num_groups     0 .. 16 (0: same as pa_decode)
+ *   workspace      at least pa_decode_shared_prefix_workspace_bytes(..., max
+ *                  shared_blocks) bytes, 256-byte aligned
+ *   others         as in pa_decode
+ *
+ * The grouped reading applies with F16/BF16 queries, G in {4, 8, 16} and the
+ * balanced schedule (num_seqs <= 1024); elsewhere the groups are ignored and
+ * every block is read per sequence. The host validates the group list
+ * (PA_ERR_SHAPE); that the tables agree and that the contexts are long
+ * enough cannot be checked on the host: if they do not, the affected
+ * sequences get meaningless values, never an out-of-bounds access.
+ */
+int pa_decode_shared_prefix(void* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* context_lens, float scale,
+                            int num_kv_heads, int block_size, int num_seqs, int num_heads, int head_size,
+                            int max_blocks_per_seq, int64_t num_blocks, pa_dtype q_dtype, pa_dtype cache_dtype,
+                            pa_dtype out_dtype, float k_scale, float v_scale, const int32_t* prefix_groups,
+                            int num_groups, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace pa_decode_shared_prefix needs when no group shares more than
+ * max_shared_blocks blocks: pa_decode_workspace_bytes(..., 0) or, where the
+ * grouped reading can apply, the balanced schedule's need plus num_seqs ints
+ * and num_heads * num_seqs * ceil(max_shared_blocks / 64) * (head_size + 2)
+ * floats of per-part results. 0 for invalid shapes.
+ */
+size_t pa_decode_shared_prefix_workspace_bytes(int num_seqs, int num_heads, int num_kv_heads, int head_size,
+                                               int max_blocks_per_seq, int block_size, int max_shared_blocks);
 
 /* Partition length (in blocks) pa_decode would choose for these shapes. */
 int pa_decode_partition_blocks(int num_seqs, int num_heads, int num_kv_heads, int head_size,

@@ -21,6 +21,7 @@ STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_DTYPE", 3: "PA_ERR_SHAPE", 4:
           5: "PA_ERR_WORKSPACE", 6: "PA_ERR_LAUNCH", 7: "PA_ERR_CAPACITY", 8: "PA_ERR_STATE"}
 
 EXPORTS = ("pa_reshape_and_cache", "pa_decode", "pa_decode_split", "pa_decode_workspace_bytes",
+           "pa_decode_shared_prefix", "pa_decode_shared_prefix_workspace_bytes",
            "pa_decode_partition_blocks", "pa_prefill", "pa_copy_blocks", "pa_bm_create", "pa_bm_destroy", "pa_bm_num_free_blocks",
            "pa_bm_block_refcount", "pa_bm_add_sequence", "pa_bm_fork", "pa_bm_free_sequence", "pa_bm_append_slots",
            "pa_bm_block_tables", "pa_last_error", "pa_version")
@@ -56,6 +57,10 @@ def load(path: str | None = None) -> ctypes.CDLL:
         lib.pa_decode.restype = _i32
         lib.pa_decode_split.argtypes = dec + [_i32, _vp, _sz, _vp]
         lib.pa_decode_split.restype = _i32
+        lib.pa_decode_shared_prefix.argtypes = dec + [_vp, _i32, _vp, _sz, _vp]
+        lib.pa_decode_shared_prefix.restype = _i32
+        lib.pa_decode_shared_prefix_workspace_bytes.argtypes = [_i32] * 7
+        lib.pa_decode_shared_prefix_workspace_bytes.restype = _sz
         lib.pa_decode_workspace_bytes.argtypes = [_i32] * 7
         lib.pa_decode_workspace_bytes.restype = _sz
         lib.pa_decode_partition_blocks.argtypes = [_i32] * 6
@@ -194,6 +199,49 @@ def decode(out, q, k_cache, v_cache, block_tables, context_lens, scale: float, n
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens), float(scale),
         num_kv_heads, block_size, S, H, D, M, N, _dtype(q), _dtype(k_cache), _dtype(out), float(k_scale),
         float(v_scale), int(partition_blocks), ws_ptr, ws_bytes, _stream(q, stream)))
+    return out
+
+
+def shared_prefix_workspace_bytes(num_seqs: int, num_heads: int, num_kv_heads: int, head_size: int,
+                                  max_blocks_per_seq: int, max_shared_blocks: int, block_size: int = 16) -> int:
+    lib = load()
+    return int(lib.pa_decode_shared_prefix_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_size,
+                                                           max_blocks_per_seq, block_size, max_shared_blocks))
+
+
+def decode_shared_prefix(out, q, k_cache, v_cache, block_tables, context_lens, scale: float, num_kv_heads: int,
+                         prefix_groups, block_size: int = 16, k_scale: float = 1.0, v_scale: float = 1.0,
+                         workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """pa_decode where groups of sequences share their first blocks: ``prefix_groups`` is a list of
+    (first_seq, num_seqs, shared_blocks) triples (kept on the host); the shared blocks are read once per
+    16 / (num_heads / num_kv_heads) sequences of a group. Same result as :func:`decode`."""
+    lib = load()
+    for t in (out, q, k_cache, v_cache, block_tables, context_lens):
+        _need(t.is_cuda and t.is_contiguous(), "all tensors must be contiguous device tensors")
+    _need(q.dim() == 3 and out.shape == q.shape, "q/out must be [S, H, D] of one shape")
+    _need(k_cache.dim() == 4 and v_cache.shape == k_cache.shape and k_cache.dtype == v_cache.dtype,
+          "caches must be [N, Hkv, B, D] of one shape and dtype")
+    _need(block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32,
+          "block_tables and context_lens must be int32")
+    S, H, D = q.shape
+    _need(block_tables.dim() == 2 and block_tables.shape[0] == S and context_lens.shape == (S,),
+          "block_tables must be [S, M] and context_lens [S]")
+    N, Hkv, B, D2 = k_cache.shape
+    _need(Hkv == num_kv_heads and B == block_size and D2 == D, "cache shape does not match the arguments")
+    M = block_tables.shape[1]
+    groups = [tuple(int(x) for x in g) for g in prefix_groups]
+    _need(all(len(g) == 3 for g in groups), "prefix_groups must hold (first_seq, num_seqs, shared_blocks) triples")
+    flat = (ctypes.c_int32 * max(1, 3 * len(groups)))(*[x for g in groups for x in g])
+    if workspace is None:
+        max_shared = max([g[2] for g in groups], default=0)
+        nbytes = shared_prefix_workspace_bytes(S, H, num_kv_heads, D, M, min(max(max_shared, 0), M), block_size)
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device) if nbytes else None
+    ws_ptr = _ptr(workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib, lib.pa_decode_shared_prefix(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens), float(scale),
+        num_kv_heads, block_size, S, H, D, M, N, _dtype(q), _dtype(k_cache), _dtype(out), float(k_scale),
+        float(v_scale), ctypes.cast(flat, _vp), len(groups), ws_ptr, ws_bytes, _stream(q, stream)))
     return out
 
 

@@ -115,6 +115,28 @@ Layout balanced_layout(int num_seqs, int num_heads, int head_size, int64_t range
   return L;
 }
 
+// Shared-prefix pass: after the balanced schedule's workspace (at offset
+// base), [S] ints of shared block counts, then [H, S, P1, D] and
+// [H, S, P1, 2] floats of per-part partial results, each 256-byte aligned.
+struct PrefixLayout {
+  size_t shared_offset, out_offset, ml_offset, total;
+};
+
+PrefixLayout prefix_layout(size_t base, int num_seqs, int num_heads, int head_size, int parts) {
+  PrefixLayout P{};
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  P.shared_offset = up(base);
+  P.out_offset = up(P.shared_offset + (size_t)num_seqs * sizeof(int));
+  const size_t rows = (size_t)num_heads * num_seqs * parts;
+  P.ml_offset = up(P.out_offset + rows * head_size * sizeof(float));
+  P.total = P.ml_offset + rows * 2 * sizeof(float);
+  return P;
+}
+
+int prefix_parts_for(int shared_blocks) {
+  return (shared_blocks + pa::kPrefixPartBlocks - 1) / pa::kPrefixPartBlocks;
+}
+
 Layout workspace_layout(int num_seqs, int num_heads, int head_size, int max_blocks, int pb) {
   Layout L{};
   L.partition_blocks = pb;
@@ -268,12 +290,17 @@ size_t pa_decode_workspace_bytes(int num_seqs, int num_heads, int num_kv_heads, 
   return split > balanced ? split : balanced;
 }
 
-int pa_decode_split(void* out, const void* q, const void* k_cache, const void* v_cache,
-                    const int32_t* block_tables, const int32_t* context_lens, float scale,
-                    int num_kv_heads, int block_size, int num_seqs, int num_heads, int head_size,
-                    int max_blocks_per_seq, int64_t num_blocks, pa_dtype q_dtype,
-                    pa_dtype cache_dtype, pa_dtype out_dtype, float k_scale, float v_scale,
-                    int partition_blocks, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// pa_decode_split and pa_decode_shared_prefix: validation, schedule choice, launch.
+// groups (host, [num_groups][3]) name the shared-prefix groups, or are NULL.
+int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                const int32_t* context_lens, float scale, int num_kv_heads, int block_size, int num_seqs,
+                int num_heads, int head_size, int max_blocks_per_seq, int64_t num_blocks, pa_dtype q_dtype,
+                pa_dtype cache_dtype, pa_dtype out_dtype, float k_scale, float v_scale, int partition_blocks,
+                const int32_t* groups, int num_groups, void* workspace, size_t workspace_bytes, void* stream) {
   if (block_size != 16) return fail(PA_ERR_UNSUPPORTED, "decode: block_size must be 16 (got %d)", block_size);
   if (head_size != 64 && head_size != 128)
     return fail(PA_ERR_UNSUPPORTED, "decode: head_size must be 64 or 128 (got %d)", head_size);
@@ -299,6 +326,21 @@ int pa_decode_split(void* out, const void* q, const void* k_cache, const void* v
       (partition_blocks < 4 || partition_blocks > pa::kMaxPartitionBlocks || partition_blocks % 4))
     return fail(PA_ERR_UNSUPPORTED, "decode: partition_blocks must be 0 or a multiple of 4 in [4, %d] (got %d)",
                 pa::kMaxPartitionBlocks, partition_blocks);
+  if (num_groups < 0 || num_groups > pa::kMaxPrefixGroups)
+    return fail(PA_ERR_SHAPE, "decode: num_groups must be in [0, %d] (got %d)", pa::kMaxPrefixGroups, num_groups);
+  if (num_groups > 0 && !groups) return fail(PA_ERR_NULL, "decode: NULL prefix_groups with num_groups > 0");
+  int max_shared = 0;
+  for (int i = 0; i < num_groups; ++i) {
+    const int first = groups[3 * i], count = groups[3 * i + 1], blocks = groups[3 * i + 2];
+    const int prev_end = i ? groups[3 * (i - 1)] + groups[3 * (i - 1) + 1] : 0;
+    if (first < prev_end || count < 1 || (int64_t)first + count > num_seqs || blocks < 1 ||
+        blocks > max_blocks_per_seq)
+      return fail(PA_ERR_SHAPE,
+                  "decode: prefix group %d (first %d, count %d, blocks %d) must lie in [0, %d) after the previous "
+                  "group, with 1 <= blocks <= %d",
+                  i, first, count, blocks, num_seqs, max_blocks_per_seq);
+    if (blocks > max_shared) max_shared = blocks;
+  }
   if (num_seqs == 0) return ok();
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
     return fail(PA_ERR_NULL, "decode: NULL pointer argument");
@@ -320,12 +362,19 @@ int pa_decode_split(void* out, const void* q, const void* k_cache, const void* v
   const Layout L = balanced ? balanced_layout(num_seqs, num_heads, head_size, ranges)
                             : workspace_layout(num_seqs, num_heads, head_size, max_blocks_per_seq, pb);
   if (L.num_parts > 65535) return fail(PA_ERR_UNSUPPORTED, "decode: too many partitions (%d)", L.num_parts);
-  if (L.total > 0) {
+  // The shared-prefix pass runs with the balanced schedule when the group
+  // size divides the 16 query columns of its tile; otherwise every block is
+  // read per sequence, which gives the same result.
+  const bool prefix = num_groups > 0 && balanced && group >= 4 && 16 % group == 0;
+  const int prefix_parts = prefix ? prefix_parts_for(max_shared) : 0;
+  const PrefixLayout PL = prefix_layout(L.total, num_seqs, num_heads, head_size, prefix_parts);
+  const size_t need = prefix ? PL.total : L.total;
+  if (need > 0) {
     if (!workspace)
-      return fail(PA_ERR_WORKSPACE, "decode: a workspace of %zu bytes is needed", L.total);
-    if (workspace_bytes < L.total)
+      return fail(PA_ERR_WORKSPACE, "decode: a workspace of %zu bytes is needed", need);
+    if (workspace_bytes < need)
       return fail(PA_ERR_WORKSPACE, "decode: workspace of %zu bytes is smaller than the %zu needed", workspace_bytes,
-                  L.total);
+                  need);
     if (reinterpret_cast<uintptr_t>(workspace) % 256)
       return fail(PA_ERR_WORKSPACE, "decode: workspace must be 256-byte aligned");
   }
@@ -357,9 +406,72 @@ int pa_decode_split(void* out, const void* q, const void* k_cache, const void* v
   a.partition_blocks = pb;
   a.num_parts = L.num_parts;
   a.out_kind = out_dtype;
+  if (prefix) {
+    char* ws = static_cast<char*>(workspace);
+    a.shared_prefix = 1;
+    a.prefix_groups = num_groups;
+    a.prefix_parts = prefix_parts;
+    a.ws_shared = reinterpret_cast<int*>(ws + PL.shared_offset);
+    a.ws_sh_out = reinterpret_cast<float*>(ws + PL.out_offset);
+    a.ws_sh_ml = reinterpret_cast<float*>(ws + PL.ml_offset);
+    const int spt = 16 / group;  // sequences per tile of the prefix pass
+    int tiles = 0;
+    for (int i = 0; i < num_groups; ++i) {
+      a.grp_first[i] = groups[3 * i];
+      a.grp_count[i] = groups[3 * i + 1];
+      a.grp_blocks[i] = groups[3 * i + 2];
+      a.grp_tile0[i] = tiles;
+      tiles += (groups[3 * i + 1] + spt - 1) / spt;
+    }
+    a.grp_tile0[num_groups] = tiles;
+    if (prefix_parts > 65535) return fail(PA_ERR_UNSUPPORTED, "decode: shared prefix too long");
+  }
   const hipError_t e = pa::launch_decode(a, q_dtype, cache_dtype, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "decode: launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_decode_split(void* out, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* context_lens, float scale,
+                    int num_kv_heads, int block_size, int num_seqs, int num_heads, int head_size,
+                    int max_blocks_per_seq, int64_t num_blocks, pa_dtype q_dtype,
+                    pa_dtype cache_dtype, pa_dtype out_dtype, float k_scale, float v_scale,
+                    int partition_blocks, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, scale, num_kv_heads, block_size, num_seqs,
+                     num_heads, head_size, max_blocks_per_seq, num_blocks, q_dtype, cache_dtype, out_dtype, k_scale,
+                     v_scale, partition_blocks, nullptr, 0, workspace, workspace_bytes, stream);
+}
+
+int pa_decode_shared_prefix(void* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* context_lens, float scale,
+                            int num_kv_heads, int block_size, int num_seqs, int num_heads, int head_size,
+                            int max_blocks_per_seq, int64_t num_blocks, pa_dtype q_dtype, pa_dtype cache_dtype,
+                            pa_dtype out_dtype, float k_scale, float v_scale, const int32_t* prefix_groups,
+                            int num_groups, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, scale, num_kv_heads, block_size, num_seqs,
+                     num_heads, head_size, max_blocks_per_seq, num_blocks, q_dtype, cache_dtype, out_dtype, k_scale,
+                     v_scale, 0, prefix_groups, num_groups, workspace, workspace_bytes, stream);
+}
+
+size_t pa_decode_shared_prefix_workspace_bytes(int num_seqs, int num_heads, int num_kv_heads, int head_size,
+                                               int max_blocks_per_seq, int block_size, int max_shared_blocks) {
+  const size_t base = pa_decode_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_size, max_blocks_per_seq,
+                                                block_size, 0);
+  if (!shapes_ok(num_seqs, num_heads, num_kv_heads, head_size, max_blocks_per_seq, block_size) ||
+      max_shared_blocks < 0 || max_shared_blocks > max_blocks_per_seq)
+    return 0;
+  if (max_shared_blocks == 0 || !balanced_tile(num_heads / num_kv_heads) ||
+      !balanced_fits(num_seqs, max_blocks_per_seq) || num_seqs == 0)
+    return base;
+  // The balanced layout for the larger (FP8) range count, then the prefix region.
+  const size_t bal = balanced_layout(num_seqs, num_heads, head_size,
+                                     balanced_ranges(num_heads, balanced_tile(num_heads / num_kv_heads), true)).total;
+  const size_t total = prefix_layout(bal, num_seqs, num_heads, head_size, prefix_parts_for(max_shared_blocks)).total;
+  return total > base ? total : base;
 }
 
 int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,

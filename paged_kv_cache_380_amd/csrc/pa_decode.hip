@@ -645,8 +645,11 @@ __global__ __launch_bounds__(64) void decode_reduce(const DecodeArgs a) {
 
 // Merge the pieces of every (sequence, head) that the balanced schedule of
 // the matrix-core kernel cut: ranges r_lo .. r_hi (those of them that hold
-// any block) each left one piece in slot seq + r. Sequences held by a single
-// range were written by the kernel itself; empty ones get zeros here.
+// any block) each left one piece in slot seq + r. With the shared-prefix
+// pass, a sequence inside a group also has one part per kPrefixPartBlocks
+// shared blocks, merged in after the pieces. Sequences held by a single
+// range and outside every group were written by the kernel itself; empty
+// ones get zeros here.
 template <int D>
 __global__ __launch_bounds__(64) void decode_bal_reduce(const DecodeArgs a) {
   __shared__ float s_f[64];
@@ -657,7 +660,8 @@ __global__ __launch_bounds__(64) void decode_bal_reduce(const DecodeArgs a) {
   const int pe = a.ws_pref[seq + 1];
   const int64_t T = a.ws_pref[a.num_seqs];
   const int64_t sh = (int64_t)seq * a.num_heads + h;
-  if (ps >= pe) {
+  const int shb = a.shared_prefix ? a.ws_shared[seq] : 0;  // shared blocks, merged from the prefix pass
+  if (ps >= pe && shb <= 0) {
 #pragma unroll
     for (int k = 0; k < D / 64; ++k) store_out(a, sh * D + lane + 64 * k, 0.f);
     return;
@@ -666,10 +670,13 @@ __global__ __launch_bounds__(64) void decode_bal_reduce(const DecodeArgs a) {
   // r_hi are the last ranges starting at or before the first and the last
   // block of the sequence.
   const int64_t R = a.ranges;
-  const int r_lo = (int)(((int64_t)(ps + 1) * R + T - 1) / T) - 1;
-  const int r_hi = (int)(((int64_t)pe * R + T - 1) / T) - 1;
-  if (r_lo >= r_hi) return;
-  const int pieces = r_hi - r_lo + 1;
+  int r_lo = 0, pieces = 0;
+  if (ps < pe) {
+    r_lo = (int)(((int64_t)(ps + 1) * R + T - 1) / T) - 1;
+    const int r_hi = (int)(((int64_t)pe * R + T - 1) / T) - 1;
+    pieces = r_hi - r_lo + 1;
+  }
+  if (pieces <= 1 && shb <= 0) return;
   const int64_t slots = (int64_t)a.num_seqs + R;
   const float* ml = a.ws_ml + ((int64_t)h * slots + seq + r_lo) * 2;
   const float* o = a.ws_out + ((int64_t)h * slots + seq + r_lo) * D;
@@ -678,7 +685,9 @@ __global__ __launch_bounds__(64) void decode_bal_reduce(const DecodeArgs a) {
 #pragma unroll
   for (int k = 0; k < D / 64; ++k) O[k] = 0.f;
   float M = kNegInf, L = 0.f;
-  if (pieces <= 64) {
+  if (pieces == 0) {
+    // Nothing past the shared prefix.
+  } else if (pieces <= 64) {
     // Common case, one round of loads: lane i takes piece i's max and sum,
     // every lane its columns of the first kPre pieces' outputs; the weights
     // are then shared by lane reads.
@@ -743,6 +752,28 @@ __global__ __launch_bounds__(64) void decode_bal_reduce(const DecodeArgs a) {
       }
     }
   }
+  if (shb > 0) {
+    // The prefix pass's parts: rescale what the pieces gave to the joint max.
+    const int np = (shb + kPrefixPartBlocks - 1) / kPrefixPartBlocks;
+    const int64_t p0 = ((int64_t)h * a.num_seqs + seq) * a.prefix_parts;
+    const float* pml = a.ws_sh_ml + 2 * p0;
+    const float* po = a.ws_sh_out + p0 * D;
+    float Mp = kNegInf;
+    for (int i = lane; i < np; i += 64) Mp = fmaxf(Mp, pml[2 * i]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) Mp = fmaxf(Mp, __shfl_xor(Mp, off, 64));
+    const float Mn = fmaxf(M, Mp);
+    const float fo = M == kNegInf ? 0.f : fast_exp2(M - Mn);
+    L *= fo;
+#pragma unroll
+    for (int k = 0; k < D / 64; ++k) O[k] *= fo;
+    for (int i = 0; i < np; ++i) {
+      const float f = fast_exp2(pml[2 * i] - Mn);
+      L += pml[2 * i + 1] * f;
+#pragma unroll
+      for (int k = 0; k < D / 64; ++k) O[k] += po[(int64_t)i * D + lane + 64 * k] * f;
+    }
+  }
 #pragma unroll
   for (int k = 0; k < D / 64; ++k) store_out(a, sh * D + lane + 64 * k, O[k] / L);
 }
@@ -781,6 +812,10 @@ hipError_t launch_d(const DecodeArgs& a, hipStream_t stream) {
 
 hipError_t launch_decode(const DecodeArgs& a, int q_kind, int cache_kind, hipStream_t stream) {
   hipError_t e;
+  if (a.shared_prefix) {
+    e = launch_decode_prefix(a, q_kind, cache_kind, stream);
+    if (e != hipSuccess) return e;
+  }
   if (a.use_mfma) {
     e = launch_decode_mfma(a, q_kind, cache_kind, stream);
   } else {

@@ -119,13 +119,14 @@ template <int CK> __device__ __forceinline__ constexpr int k_col(int b, int g) {
   return CK == kFP8 ? 64 * (b >> 1) + 16 * g + 8 * (b & 1) : 32 * b + 8 * g;
 }
 
-template <int QK, int CK, int D, int GT, bool kShared, bool kBalanced>
+template <int QK, int CK, int D, int GT, bool kShared, bool kBalanced, bool kPrefix = false>
 __global__ __launch_bounds__(kThreads) void decode_mfma(const DecodeArgs a) {
   using G = MGeo<CK, D>;
   constexpr int NKB = G::NKB, NKL = G::NKL, NVL = G::NVL, NDB = G::NDB, VS = G::kVStride;
   static_assert(QK == kF16 || QK == kBF16, "16-bit queries");
   static_assert(GT == 4 || GT == 8 || GT == 16 || (GT == 32 && kBalanced),
                 "head tile of 4, 8 or 16; 32 (two sub-tiles per wave) in the balanced schedule only");
+  static_assert(!kPrefix || (GT == 16 && !kBalanced && !kShared), "the shared-prefix pass takes 16 columns");
   constexpr int NT = GT > 16 ? GT / 16 : 1;  // 16-head sub-tiles of a wave, sharing each K/V tile
   constexpr int GS = GT > 16 ? 16 : GT;      // heads per sub-tile
 
@@ -134,9 +135,10 @@ __global__ __launch_bounds__(kThreads) void decode_mfma(const DecodeArgs a) {
   __shared__ float s_acc[kBalanced ? 1 : kWaves * GT * D];
   __shared__ float s_ml[kBalanced ? 1 : kWaves * GT * 2];
   __shared__ int s_pref[kBalanced ? kBalancedMaxSeqs + 1 : 1];
+  __shared__ int s_shr[kBalanced ? kBalancedMaxSeqs : 1];  // shared-prefix blocks of each sequence
   __shared__ int s_scan[kBalanced ? kWaves : 1];
 
-  const int n_sub = a.group / GT;
+  const int n_sub = kPrefix ? 1 : a.group / GT;  // the prefix pass: x is the KV head
   int bx, part, seq;  // balanced: part is the group of four ranges, seq is set per piece
   wg_coords<kShared>(bx, part, seq);
   const int kvh = bx / n_sub;
@@ -405,7 +407,92 @@ __global__ __launch_bounds__(kThreads) void decode_mfma(const DecodeArgs a) {
     }
   };
 
-  if constexpr (!kBalanced) {
+  if constexpr (kPrefix) {
+    // Shared-prefix pass: workgroup (KV head, part, tile). The tile's 16
+    // query columns are the (sequence, head) pairs of 16 / group consecutive
+    // sequences of one group, which share the group's first blocks, so every
+    // shared K/V tile is read once for all of them (their table rows agree
+    // there; the first sequence's row is read). All shared blocks are full:
+    // no row is masked. Each column leaves the part's max, sum and
+    // unnormalised output for decode_bal_reduce.
+    const int tile = seq;
+    const int S = a.num_seqs;
+    if (kvh == 0 && part == 0 && tile == 0) {  // the per-sequence shared block counts, for the kernels after
+      for (int s = tid; s < S; s += kThreads) {
+        int shb = 0;
+        for (int gi = 0; gi < a.prefix_groups; ++gi)
+          if (s >= a.grp_first[gi] && s < a.grp_first[gi] + a.grp_count[gi]) shb = a.grp_blocks[gi];
+        a.ws_shared[s] = shb;
+      }
+    }
+    int gi = 0;
+    while (gi + 1 < a.prefix_groups && tile >= a.grp_tile0[gi + 1]) ++gi;
+    const int spt = 16 / a.group;  // sequences per tile
+    const int s0 = a.grp_first[gi] + (tile - a.grp_tile0[gi]) * spt;
+    const int s_end = min(a.grp_first[gi] + a.grp_count[gi], s0 + spt);
+    const int nshared = a.grp_blocks[gi];
+    blk0 = part * kPrefixPartBlocks;
+    if (blk0 >= nshared || s0 >= s_end) return;
+    const int nblk = min(kPrefixPartBlocks, nshared - blk0);
+    ctx = nshared * 16;
+    const int32_t* bt = a.block_tables + (int64_t)a.grp_first[gi] * a.max_blocks + blk0;
+    for (int j = tid; j < nblk; j += kThreads) s_blocks[j] = bt[j];
+    // Column n: query head kvh * group + n % group of sequence s0 + n / group
+    // (zero past the group's last sequence; such columns are not written).
+    const int cs = s0 + n / a.group;
+    {
+      const char* qp = static_cast<const char*>(a.q) +
+                       ((int64_t)cs * a.num_heads + kvh * a.group + n % a.group) * D * 2;
+#pragma unroll
+      for (int b = 0; b < NKB; ++b) {
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (cs < s_end) v = *reinterpret_cast<const uint4*>(qp + k_col<CK>(b, g) * 2);
+        qf[0][b][0] = v.x;
+        qf[0][b][1] = v.y;
+        qf[0][b][2] = v.z;
+        qf[0][b][3] = v.w;
+      }
+    }
+    __syncthreads();
+
+    reset();
+    run_blocks(wave, kWaves, nblk, nshared);
+
+    float ls = lsum[0] + __shfl_xor(lsum[0], 16, 64);
+    ls += __shfl_xor(ls, 32, 64);
+    if (g == 0) {
+      s_ml[(wave * 16 + n) * 2] = mref[0];
+      s_ml[(wave * 16 + n) * 2 + 1] = ls;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) s_acc[(wave * 16 + 4 * g + i) * D + db * 16 + n] = acc[0][db][i];
+    __syncthreads();
+    // Merge the waves per column (the part holds a block, so the max is finite).
+    for (int idx = tid; idx < 16 * D; idx += kThreads) {
+      const int c = idx / D;
+      const int d = idx - c * D;
+      const int s = s0 + c / a.group;
+      if (s >= s_end) continue;
+      float M = kNegInf;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_ml[(w * 16 + c) * 2]);
+      float Lw = 0.f, O = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float f = fast_exp2(s_ml[(w * 16 + c) * 2] - M);
+        Lw += s_ml[(w * 16 + c) * 2 + 1] * f;
+        O += s_acc[(w * 16 + c) * D + d] * f;
+      }
+      const int64_t pi = ((int64_t)(kvh * a.group + c % a.group) * S + s) * a.prefix_parts + part;
+      a.ws_sh_out[pi * D + d] = O * a.out_scale;
+      if (d == 0) {
+        a.ws_sh_ml[2 * pi] = M;
+        a.ws_sh_ml[2 * pi + 1] = Lw;
+      }
+    }
+  } else if constexpr (!kBalanced) {
     // One partition of one sequence; the four waves take its blocks in turn.
     ctx = context_len(a, seq);
     if (ctx <= 0) {
@@ -462,9 +549,14 @@ __global__ __launch_bounds__(kThreads) void decode_mfma(const DecodeArgs a) {
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const int s = tid * per + k;
-      int c = 0;
-      if (k < per && s < S) c = context_len(a, s);
-      nb[k] = c > 0 ? (c + 15) >> 4 : 0;
+      int c = 0, shb = 0;
+      if (k < per && s < S) {
+        c = context_len(a, s);
+        if (a.shared_prefix) shb = a.ws_shared[s];
+        s_shr[s] = shb;
+      }
+      // Blocks past the shared prefix (those inside it were read by the prefix pass).
+      nb[k] = c > 0 ? max(0, ((c + 15) >> 4) - shb) : 0;
       local += nb[k];
     }
     // Inclusive scan of the per-thread sums: within each wave by shuffles,
@@ -517,7 +609,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma(const DecodeArgs a) {
       for (int i = lane; i < to - from; i += 64) {
         const int p = from + i;
         const int s = seq_of(p);
-        wblocks[i] = a.block_tables[(int64_t)s * a.max_blocks + (p - s_pref[s])];
+        wblocks[i] = a.block_tables[(int64_t)s * a.max_blocks + (p - s_pref[s]) + s_shr[s]];
       }
       wave_lds_fence();
       win = from;
@@ -531,6 +623,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma(const DecodeArgs a) {
       seq = __builtin_amdgcn_readfirstlane(seq_of(pos));
       const int ps = s_pref[seq], pe = s_pref[seq + 1];
       const int piece_end = min(r_end, pe);
+      const int shb = s_shr[seq];  // position ps is block shb of the sequence
       ctx = context_len(a, seq);
       load_q(seq);
       reset();
@@ -538,13 +631,14 @@ __global__ __launch_bounds__(kThreads) void decode_mfma(const DecodeArgs a) {
       for (int sub = pos; sub < piece_end;) {
         if (sub >= win_end) stage(sub, min(sub + kWindow, r_end));
         const int sub_end = min(piece_end, win_end);
-        blk0 = sub - ps;
+        blk0 = sub - ps + shb;
         sb_off = sub - win;
-        run_blocks(0, 1, sub_end - sub, pe - ps);
+        run_blocks(0, 1, sub_end - sub, pe - ps + shb);
         sub = sub_end;
       }
 
-      const bool whole = pos == ps && piece_end == pe;
+      // A sequence with a shared prefix always leaves a piece: the merge adds the prefix pass's parts.
+      const bool whole = pos == ps && piece_end == pe && shb == 0;
       const int64_t slot = seq + r;
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
@@ -625,7 +719,28 @@ hipError_t launch_d(const DecodeArgs& a, hipStream_t stream) {
   }
 }
 
+template <int QK, int CK>
+hipError_t launch_prefix_d(const DecodeArgs& a, hipStream_t stream) {
+  const dim3 grid((unsigned)a.num_kv_heads, (unsigned)a.prefix_parts, (unsigned)a.grp_tile0[a.prefix_groups]);
+  switch (a.head_size) {
+    case 64: decode_mfma<QK, CK, 64, 16, false, false, true><<<grid, dim3(kThreads), 0, stream>>>(a); break;
+    case 128: decode_mfma<QK, CK, 128, 16, false, false, true><<<grid, dim3(kThreads), 0, stream>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_decode_prefix(const DecodeArgs& a, int q_kind, int cache_kind, hipStream_t stream) {
+  switch (q_kind * 4 + cache_kind) {
+    case kF16 * 4 + kF16: return launch_prefix_d<kF16, kF16>(a, stream);
+    case kBF16 * 4 + kBF16: return launch_prefix_d<kBF16, kBF16>(a, stream);
+    case kF16 * 4 + kFP8: return launch_prefix_d<kF16, kFP8>(a, stream);
+    case kBF16 * 4 + kFP8: return launch_prefix_d<kBF16, kFP8>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, int q_kind, int cache_kind, hipStream_t stream) {
   switch (q_kind * 4 + cache_kind) {

@@ -25,6 +25,10 @@ struct ReshapeArgs {
 // Returns a hipError_t of the launch.
 hipError_t launch_reshape(const ReshapeArgs& a, int src_kind, int cache_kind, hipStream_t stream);
 
+// Groups a shared-prefix call may name, and blocks per part of the prefix kernel.
+constexpr int kMaxPrefixGroups = 16;
+constexpr int kPrefixPartBlocks = 64;
+
 struct DecodeArgs {
   void* out;
   const void* q;
@@ -52,12 +56,30 @@ struct DecodeArgs {
   int use_mfma;           // 1: matrix-core kernel (16-bit queries, group_tile 4, 8 or 16)
   int balanced;           // 1: balanced schedule (matrix-core kernel only): equal block ranges per wave
   int ranges;             // balanced schedule: number of ranges R (a multiple of 4)
+  // Shared-prefix pass (balanced schedule only): groups of consecutive
+  // sequences whose block tables start with the same full blocks. The prefix
+  // kernel reads those blocks once per 16 query columns (16 / group sequences)
+  // and leaves per-part partial results; the balanced kernel then streams
+  // only the blocks past each sequence's shared prefix.
+  int shared_prefix;      // 1: the pass runs (ws_shared, ws_sh_* and the group list are set)
+  int prefix_groups;      // number of groups (<= kMaxPrefixGroups)
+  int prefix_parts;       // P1: parts of kPrefixPartBlocks blocks of the longest shared prefix
+  int* ws_shared;         // [S] shared blocks of each sequence (0 outside every group)
+  float* ws_sh_out;       // [H, S, P1, D] unnormalised partial outputs over the shared blocks
+  float* ws_sh_ml;        // [H, S, P1, 2] their max (log2 domain) and sum
+  int grp_first[kMaxPrefixGroups];  // group g: sequences grp_first[g] .. grp_first[g] + grp_count[g] - 1
+  int grp_count[kMaxPrefixGroups];
+  int grp_blocks[kMaxPrefixGroups];     // shared full blocks of group g
+  int grp_tile0[kMaxPrefixGroups + 1];  // first prefix-kernel tile of group g (tiles of 16 / group sequences)
 };
+
 
 // Queues the decode kernel(s) chosen by a.use_mfma, then the partition merge if needed.
 hipError_t launch_decode(const DecodeArgs& a, int q_kind, int cache_kind, hipStream_t stream);
 // The matrix-core decode kernel alone (pa_decode_mfma.hip).
 hipError_t launch_decode_mfma(const DecodeArgs& a, int q_kind, int cache_kind, hipStream_t stream);
+// The shared-prefix pass of the matrix-core kernel (a.shared_prefix; 16-bit queries, group 4, 8 or 16).
+hipError_t launch_decode_prefix(const DecodeArgs& a, int q_kind, int cache_kind, hipStream_t stream);
 
 // Largest query-head tile (8, 4, 2 or 1) dividing the group size.
 inline int group_tile_for(int group) {

@@ -67,6 +67,7 @@ class Workload:
     new_value: torch.Tensor
     new_slots: torch.Tensor       # int64 [S], -1 for a sequence with no tokens
     shared_blocks: int = 0
+    sharing_seqs: int = 0         # sequences 0 .. sharing_seqs - 1 share the first shared_blocks blocks
     seed: int = 0
     meta: dict = field(default_factory=dict)
 
@@ -175,7 +176,8 @@ def build(name: str, context_lens, num_heads: int, num_kv_heads: int, head_size:
         block_tables=torch.from_numpy(tables.astype(np.int32)),
         q=q, fill_key=fill_key, fill_value=fill_value, fill_slots=torch.from_numpy(fill_slots),
         new_key=new_key, new_value=new_value, new_slots=torch.from_numpy(new_slots),
-        shared_blocks=shared_prefix_blocks if sharing_seqs else 0, seed=seed,
+        shared_blocks=shared_prefix_blocks if sharing_seqs else 0,
+        sharing_seqs=sharing_seqs if shared_prefix_blocks else 0, seed=seed,
         meta={"used_blocks": used},
     )
 
@@ -219,12 +221,23 @@ def prefix_fp8(seed: int = 5) -> Workload:
                  free_fraction=0.10, shared_prefix_blocks=64, sharing_seqs=128, kv_scale=0.05)
 
 
+def prefix_long_fp8(seed: int = 6) -> Workload:
+    """Long shared prompt: 256 sequences share one 4096-token prefix (256 physical blocks) and add private
+    tails of U{16..512} tokens; fp8 E4M3 cache (scale 0.05), bf16 queries, 32/8 heads, pool + 10% free.
+    Not one of the five reference shapes: it measures the shared-prefix pass where the prefix dominates."""
+    def lengths(g):
+        return (4096 + torch.randint(16, 513, (256,), generator=g)).tolist()
+    return build("prefix_long_fp8_b256", lengths, 32, 8, 128, "bf16", cache_dtype="fp8_e4m3", seed=seed,
+                 free_fraction=0.10, shared_prefix_blocks=256, sharing_seqs=256, kv_scale=0.05)
+
+
 NAMED = {
     "tiny_fp32": tiny_fp32,
     "llama7b_mha_fp16": llama7b_mha_fp16,
     "llama3_8b_gqa_bf16": llama3_8b_gqa_bf16,
     "longctx_bf16": longctx_bf16,
     "prefix_fp8": prefix_fp8,
+    "prefix_long_fp8": prefix_long_fp8,
 }
 
 

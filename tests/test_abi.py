@@ -181,3 +181,60 @@ def test_partition_choice(lib):
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(RuntimeError, match="not found"):
         binding.load(str(tmp_path / "missing.so"))
+
+
+def shared(lib, groups, **kw):
+    a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, cl=FAKE, scale=0.125, Hkv=2, B=16, S=8, H=8, D=128, M=8,
+             N=64, qd=1, cd=1, od=1, ks=1.0, vs=1.0, ws=None, wsb=0, stream=None, ng=None)
+    a.update(kw)
+    flat = (ctypes.c_int32 * max(1, 3 * len(groups)))(*[x for g in groups for x in g])
+    ng = len(groups) if a["ng"] is None else a["ng"]
+    ptr = None if a.get("null_groups") else ctypes.cast(flat, ctypes.c_void_p)
+    return lib.pa_decode_shared_prefix(a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["cl"], a["scale"], a["Hkv"],
+                                       a["B"], a["S"], a["H"], a["D"], a["M"], a["N"], a["qd"], a["cd"], a["od"],
+                                       a["ks"], a["vs"], ptr, ng, a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("groups,kw", [
+    ([(0, 4, 2)] * 17, {}),                    # more groups than the 16 a call may name
+    ([(0, 0, 2)], {}),                         # empty group
+    ([(0, 4, 0)], {}),                         # no shared block
+    ([(0, 4, 9)], {}),                         # more shared blocks than a table row holds (M = 8)
+    ([(6, 3, 2)], {}),                         # past the last sequence
+    ([(-1, 3, 2)], {}),
+    ([(0, 4, 2), (3, 2, 2)], {}),              # overlapping
+    ([(4, 2, 2), (0, 2, 2)], {}),              # out of order
+    ([(0, 4, 2)], dict(S=0)),                  # validated before the empty-batch shortcut
+])
+def test_shared_prefix_rejects_groups(lib, groups, kw):
+    assert shared(lib, groups, **kw) == 3
+    assert "prefix group" in lib.pa_last_error().decode() or "num_groups" in lib.pa_last_error().decode()
+
+
+def test_shared_prefix_null_groups(lib):
+    assert shared(lib, [(0, 4, 2)], null_groups=True) == 1
+    assert shared(lib, [], S=0, out=None, q=None) == 0  # no groups, no sequences: nothing to do
+
+
+def test_shared_prefix_workspace(lib):
+    S, H, Hkv, D, M = 8, 8, 2, 128, 8
+    base = lib.pa_decode_workspace_bytes(S, H, Hkv, D, M, 16, 0)
+    # no shared block, or a group size the grouped reading does not take (6): the plain need
+    assert lib.pa_decode_shared_prefix_workspace_bytes(S, H, Hkv, D, M, 16, 0) == base
+    assert lib.pa_decode_shared_prefix_workspace_bytes(S, 48, 8, D, M, 16, 4) == \
+        lib.pa_decode_workspace_bytes(S, 48, 8, D, M, 16, 0)
+    assert lib.pa_decode_shared_prefix_workspace_bytes(S, H, Hkv, D, M, 16, 9) == 0  # more than a row
+    # the balanced need, then S ints and H * S * P1 * (D + 2) floats, 256-aligned parts (parts of 64
+    # shared blocks: P1 = 1 for 5 blocks, 2 for 65)
+    up = lambda x: (x + 255) // 256 * 256
+    for m, shared_blocks, parts in [(M, 5, 1), (80, 65, 2)]:
+        b = lib.pa_decode_workspace_bytes(S, H, Hkv, D, m, 16, 0)
+        sh_off = up(b)
+        out_off = up(sh_off + S * 4)
+        ml_off = up(out_off + H * S * parts * D * 4)
+        need = ml_off + H * S * parts * 2 * 4
+        assert lib.pa_decode_shared_prefix_workspace_bytes(S, H, Hkv, D, m, 16, shared_blocks) == need
+    # a workspace that holds the balanced schedule but not the prefix results is refused (an FP8
+    # cache takes the range count the plain size is computed for)
+    assert shared(lib, [(0, 8, 5)], ws=FAKE, wsb=base, cd=3) == 5
+    assert "workspace" in lib.pa_last_error().decode()
