@@ -45,8 +45,9 @@ def kernel_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def counter_traffic(workload: str, algorithmic_bytes: float):
-    """HBM bytes per decode launch from the committed rocprofv3 counter summary, if it is current."""
+def counter_traffic(workload: str, shared_prefix: bool):
+    """HBM bytes per decode call from the committed rocprofv3 counter summary, if it is current (same kernel
+    sources, same use of the shared-prefix pass)."""
     path = os.path.join(PROFILES, f"decode_{workload}_counters.txt")
     if not os.path.exists(path):
         return None
@@ -57,8 +58,10 @@ def counter_traffic(workload: str, algorithmic_bytes: float):
     sha = re.search(r"^kernel_source_sha:\s*(\S+)", text, re.M)
     if not sha or sha.group(1) != kernel_source_sha():
         return None  # the kernel changed since the counters were taken
-    b = field("hbm_bytes_per_dispatch")
-    return b
+    mode = re.search(r"^shared_prefix:\s*(\S+)", text, re.M)
+    if (mode.group(1) if mode else "no") != ("yes" if shared_prefix else "no"):
+        return None
+    return field("hbm_bytes_per_call")
 
 
 def decode_algorithmic_bytes(w) -> int:
@@ -110,24 +113,29 @@ def summarize_stats(directory: str, out_path: str, command: str):
 
 
 def _counter_means(directory: str, counter: str, select) -> tuple[float, int, str]:
-    vals, names = {}, set()
+    """Per selected kernel, the mean of the counter over its dispatches; returns the sum of those means
+    (one call's worth when each selected kernel runs once per call), the dispatch count of the most
+    frequent kernel, and the kernel names."""
+    vals = {}
     for r in _csv_rows(directory, "counter_collection.csv"):
         name = _col(r, "Kernel_Name")
         if _col(r, "Counter_Name") != counter or not select(name):
             continue
+        per = vals.setdefault(_short(name), {})
         key = _col(r, "Dispatch_Id", "Correlation_Id")
-        vals[key] = vals.get(key, 0.0) + float(_col(r, "Counter_Value"))
-        names.add(_short(name))
+        per[key] = per.get(key, 0.0) + float(_col(r, "Counter_Value"))
     if not vals:
         raise SystemExit(f"no {counter} rows for the selected kernel under {directory}")
-    return sum(vals.values()) / len(vals), len(vals), ", ".join(sorted(names))
+    total = sum(sum(per.values()) / len(per) for per in vals.values())
+    return total, max(len(per) for per in vals.values()), ", ".join(sorted(vals))
 
 
 def summarize_counters(workload: str, fetch_dir: str, write_dir: str, cal_fetch_dir: str, cal_write_dir: str,
-                       copy_mib: int, out_path: str, commands: list[str]):
-    """HBM bytes per decode launch: FETCH_SIZE and WRITE_SIZE (KiB) scaled by what they read for a plain copy."""
+                       copy_mib: int, out_path: str, commands: list[str], shared_prefix_mode: str = "auto"):
+    """HBM bytes per decode call (all its kernels: prefix pass, main kernel, merge): FETCH_SIZE and
+    WRITE_SIZE (KiB) scaled by what they read for a plain copy."""
     from paged_kv_cache_380_amd import workloads as wl
-    is_decode = lambda n: "decode_main" in n or "decode_gqa" in n or "decode_mfma" in n
+    is_decode = lambda n: "decode_" in n
     is_copy = lambda n: "copy" in n.lower()
     fetch, nf, kname = _counter_means(fetch_dir, "FETCH_SIZE", is_decode)
     write, nw, _ = _counter_means(write_dir, "WRITE_SIZE", is_decode)
@@ -138,15 +146,17 @@ def summarize_counters(workload: str, fetch_dir: str, write_dir: str, cal_fetch_
     hbm = ff * fetch * 1024 + fw * write * 1024
     w = wl.named(workload)
     algo = decode_algorithmic_bytes(w)
+    prefix = shared_prefix_applies(w, 0) if shared_prefix_mode == "auto" else shared_prefix_mode == "on"
     lines = [
-        "# rocprofv3 HBM counters of the decode kernel",
+        "# rocprofv3 HBM counters of one decode call (sum over its kernels of each kernel's mean per dispatch)",
         f"workload: {w.name}", f"kernel: {kname}", f"kernel_source_sha: {kernel_source_sha()}",
+        f"shared_prefix: {'yes' if prefix else 'no'}",
         f"dispatches: {nf} (FETCH_SIZE run), {nw} (WRITE_SIZE run)",
-        f"FETCH_SIZE_KiB_per_dispatch: {fetch:.1f}", f"WRITE_SIZE_KiB_per_dispatch: {write:.1f}",
+        f"FETCH_SIZE_KiB_per_call: {fetch:.1f}", f"WRITE_SIZE_KiB_per_call: {write:.1f}",
         f"calibration_kernel: {cname} ({copy_mib} MiB read + {copy_mib} MiB written)",
         f"calibration_FETCH_SIZE_KiB: {cfetch:.1f}", f"calibration_WRITE_SIZE_KiB: {cwrite:.1f}",
         f"fetch_factor: {ff:.4f}", f"write_factor: {fw:.4f}",
-        f"hbm_bytes_per_dispatch: {hbm:.0f}", f"algorithmic_bytes_per_dispatch: {algo}",
+        f"hbm_bytes_per_call: {hbm:.0f}", f"algorithmic_bytes_per_call: {algo}",
         f"traffic_over_algorithmic: {hbm / algo:.4f}", "commands:"] + [f"  {c}" for c in commands]
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -230,7 +240,7 @@ def main():
         return
     if args.summarize_counters:
         fd, wd, cfd, cwd, mib, out = args.summarize_counters
-        summarize_counters(args.workload, fd, wd, cfd, cwd, int(mib), out, args.command)
+        summarize_counters(args.workload, fd, wd, cfd, cwd, int(mib), out, args.command, args.shared_prefix)
         return
 
     if args.gpus != 1:
@@ -327,7 +337,7 @@ def main():
     step_bytes = wl.algorithmic_step_bytes(w)
     decode_bytes = decode_algorithmic_bytes(w)
     achieved = decode_bytes / (decode_ms * 1e-3) / 1e9
-    traffic = counter_traffic(w.name, decode_bytes)
+    traffic = counter_traffic(w.name, prefix)
 
     res = {
         "metric": "paged-attn decode KV-read HBM GB/s (% of peak) + seq-steps/s, 7B shape b32",
