@@ -244,7 +244,10 @@ size_t pa_decode_workspace_bytes(int num_seqs, int num_heads, int num_kv_heads, 
  *
  * The grouped reading applies with F16/BF16 queries, G in {4, 8, 16} and the
  * balanced schedule (num_seqs <= 1024); elsewhere the groups are ignored and
- * every block is read per sequence. The host validates the group list
+ * every block is read per sequence. A workspace too small for the balanced
+ * schedule also leaves the groups unused (pa_decode's partitioned fallback);
+ * one that holds the balanced schedule but not the per-part results is
+ * refused (PA_ERR_WORKSPACE). The host validates the group list
  * (PA_ERR_SHAPE); that the tables agree and that the contexts are long
  * enough cannot be checked on the host: if they do not, the affected
  * sequences get meaningless values, never an out-of-bounds access.

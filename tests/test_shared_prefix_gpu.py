@@ -169,3 +169,18 @@ def test_prefix_long_fp8_full_size_sampled():
     ref = oracle_decode(w, kc, vc, seqs=seqs)
     got = out.cpu().numpy()[seqs]
     assert float(np.abs(got - ref[seqs]).max()) <= tolerance(w)  # the oracle fills only the sampled rows
+
+
+def test_groups_ignored_past_the_balanced_batch_and_for_float32():
+    # 1025 sequences take the partitioned schedule; float32 queries the vector-ALU kernel: the groups are
+    # ignored and the result is pa_decode's (here bit for bit: the same kernels run)
+    rng = np.random.default_rng(16)
+    w = sharing("shared_past_max", 16, 4, 64, "bf16", "bf16", 3, [int(rng.integers(1, 40)) for _ in range(6)],
+                [int(rng.integers(0, 40)) for _ in range(1019)], seed=27)
+    out, ref_gpu, ref = run_both(w, [(0, 6, 3)])
+    assert torch.equal(out, ref_gpu)
+    assert float(np.abs(out.cpu().numpy() - ref).max()) <= tolerance(w)
+    w = sharing("shared_f32", 8, 2, 64, "f32", "f32", 4, [5, 30, 70], [12, 1], seed=28)
+    out, ref_gpu, ref = run_both(w, [(0, 3, 4)])
+    assert torch.equal(out, ref_gpu)
+    assert float(np.abs(out.cpu().numpy() - ref).max()) <= tolerance(w)
