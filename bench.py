@@ -332,6 +332,22 @@ def main():
     durs = sorted(a.elapsed_time(b) for a, b in ev)
     decode_ms = sum(durs) / len(durs)
 
+    # The same launches with the caches cold: 512 MiB written before each one (outside its events)
+    # evicts the L2s and the 256 MB Infinity Cache, so nothing of the previous launch's reads is left.
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(min(args.steps, 50))]
+    for a, b in cold_ev:
+        case.append()
+        flush.fill_(1)
+        a.record(stream)
+        run_decode()
+        b.record(stream)
+    torch.cuda.synchronize()
+    cold = sorted(a.elapsed_time(b) for a, b in cold_ev)
+    decode_ms_cold = sum(cold) / len(cold)
+    del flush
+
     kv_bytes = wl.algorithmic_kv_bytes(w)
     kv_unique = wl.algorithmic_kv_bytes(w, unique=True)
     step_bytes = wl.algorithmic_step_bytes(w)
@@ -365,6 +381,7 @@ def main():
         "seq_steps_per_s": round(w.num_seqs / (ms_per_step * 1e-3), 1),
         "decode_ms": round(decode_ms, 5),
         "decode_ms_p10_p90": [round(durs[len(durs) // 10], 5), round(durs[(9 * len(durs)) // 10], 5)],
+        "decode_ms_cold_cache": round(decode_ms_cold, 5),
         "roofline": {
             "kernel": ("decode_mfma[shared prefix] + " if prefix else "") + decode_kernels(w, args.partition_blocks, pb),
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
