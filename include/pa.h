@@ -94,7 +94,8 @@ typedef enum pa_status {
  *   k_cache, v_cache device, [num_blocks, num_kv_heads, block_size, head_size], cache_dtype
  *                   (== kv_dtype, or FP8_E4M3)
  *   slot_mapping    device, [num_tokens]; int64 if slot_is_int64 else int32
- *   num_tokens      >= 0 (0 queues nothing and returns PA_OK)
+ *   num_tokens      >= 0 (0 queues nothing and returns PA_OK); num_tokens * num_kv_heads
+ *                   * head_size * sizeof(kv_dtype) / 16 below 2^31 - 256 (PA_ERR_SHAPE)
  *   block_size      must be 16; head_size must be 64 or 128
  *
  * Slots must be distinct within one call (two tokens writing one slot race).

@@ -175,6 +175,12 @@ int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void
       !(std::isfinite(k_scale) && std::isfinite(v_scale) && k_scale > 0.f && v_scale > 0.f))
     return fail(PA_ERR_SHAPE, "reshape_and_cache: FP8 scales must be finite and positive");
   if (num_tokens == 0) return ok();
+  // The kernel indexes 16-byte source chunks in 32 bits (one thread each).
+  const int64_t chunks = num_tokens * num_kv_heads * (int64_t)head_size *
+                         (kv_dtype == PA_DTYPE_F32 ? 4 : 2) / 16;
+  if (chunks + 255 > 0x7fffffffLL)
+    return fail(PA_ERR_SHAPE, "reshape_and_cache: %lld tokens of %d KV heads are too many for one call",
+                (long long)num_tokens, num_kv_heads);
   if (!key || !value || !k_cache || !v_cache || !slot_mapping)
     return fail(PA_ERR_NULL, "reshape_and_cache: NULL pointer argument");
   pa::ReshapeArgs a{key, value, k_cache, v_cache, slot_mapping, num_tokens, num_blocks, num_kv_heads, head_size,

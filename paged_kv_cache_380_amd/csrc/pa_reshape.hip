@@ -50,23 +50,25 @@ template <int SRC, int CACHE>
 __global__ __launch_bounds__(kThreads) void reshape_kernel(ReshapeArgs a) {
   constexpr int kSrcBytes = KindBytes<SRC>::value;
   constexpr int E = 16 / kSrcBytes;  // source elements per chunk
-  const int chunks_per_row = a.head_size / E;
-  const int64_t chunks_per_tok = (int64_t)a.num_kv_heads * chunks_per_row;
-  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (idx >= a.num_tokens * chunks_per_tok) return;
-  const int64_t t = idx / chunks_per_tok;
+  // The launch holds fewer than 2^31 source chunks, so the index math runs in 32 bits.
+  const uint32_t chunks_per_row = (uint32_t)(a.head_size / E);
+  const uint32_t chunks_per_tok = (uint32_t)a.num_kv_heads * chunks_per_row;
+  const uint32_t idx = blockIdx.x * kThreads + threadIdx.x;
+  if ((int64_t)idx >= a.num_tokens * (int64_t)chunks_per_tok) return;
+  const uint32_t t = idx / chunks_per_tok;
   const int rem = (int)(idx - t * chunks_per_tok);
+  // The source chunk is in bounds whatever the slot: its loads go out together
+  // with the slot's, so the kernel waits for memory once, not twice.
+  const int64_t src_elem = (int64_t)idx * E;  // == t*Hkv*D + head*D + chunk*E
+  const uint4 kv = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.key) + src_elem * kSrcBytes);
+  const uint4 vv = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.value) + src_elem * kSrcBytes);
   const int64_t slot = a.slot_is_int64 ? static_cast<const int64_t*>(a.slots)[t]
                                        : (int64_t) static_cast<const int32_t*>(a.slots)[t];
   if (slot < 0 || slot >= a.num_blocks * 16) return;  // padding, or outside the pool
-  const int head = rem / chunks_per_row;
-  const int chunk = rem - head * chunks_per_row;
+  const int head = rem / (int)chunks_per_row;
+  const int chunk = rem - head * (int)chunks_per_row;
   const int64_t blk = slot >> 4;  // block_size is 16
   const int row = (int)(slot & 15);
-
-  const int64_t src_elem = idx * E;  // == t*Hkv*D + head*D + chunk*E
-  const uint4 kv = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.key) + src_elem * kSrcBytes);
-  const uint4 vv = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.value) + src_elem * kSrcBytes);
   const int64_t dst_elem = ((blk * a.num_kv_heads + head) * 16 + row) * a.head_size + (int64_t)chunk * E;
 
   if constexpr (CACHE == SRC) {
@@ -87,7 +89,7 @@ hipError_t launch(const ReshapeArgs& a, hipStream_t stream) {
   const int64_t total = a.num_tokens * a.num_kv_heads * (a.head_size / E);
   const int64_t blocks = (total + kThreads - 1) / kThreads;
   if (blocks == 0) return hipSuccess;
-  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  if (blocks * kThreads > 0x7fffffffLL) return hipErrorInvalidConfiguration;  // 32-bit index math in the kernel
   reshape_kernel<SRC, CACHE><<<dim3((unsigned)blocks), dim3(kThreads), 0, stream>>>(a);
   return hipGetLastError();
 }

@@ -66,6 +66,7 @@ def decode(lib, split=None, **kw):
     (dict(B=8), 4), (dict(D=96), 4), (dict(T=-1), 3), (dict(Hkv=0), 3), (dict(N=0), 3),
     (dict(kvd=3), 2), (dict(kvd=1, cd=2), 2), (dict(kvd=9), 2), (dict(cd=3, ks=0.0), 3),
     (dict(cd=3, vs=float("inf")), 3), (dict(key=None), 1), (dict(slots=None), 1),
+    (dict(T=1 << 24, Hkv=8, D=128), 3),  # 2^31 source chunks of 16 bytes: past the kernel's 32-bit index
 ])
 def test_reshape_rejects(lib, kw, code):
     assert reshape(lib, **kw) == code
