@@ -105,3 +105,24 @@ def test_uniform_configs_tables_only(name, monkeypatch):
     else:
         assert w.num_blocks == 16384 and w.meta["used_blocks"] == 16384
         assert wl.algorithmic_kv_bytes(w) == 1024 ** 3
+
+
+@pytest.mark.parametrize("make,sharing,blocks", [(wl.prefix_fp8, 128, 64), (wl.prefix_long_fp8, 256, 256)])
+def test_shared_prefix_group_is_what_the_tables_hold(make, sharing, blocks):
+    # The group bench.py and the tests pass to pa_decode_shared_prefix, (0, sharing_seqs, shared_blocks), must
+    # be true of the tables: those sequences agree on their first shared_blocks entries, every one of them
+    # holds more than that many blocks' worth of tokens, and no other sequence touches those blocks.
+    w = make()
+    assert (w.sharing_seqs, w.shared_blocks) == (sharing, blocks)
+    t = w.block_tables.numpy()
+    lens = w.context_lens.numpy()
+    assert (t[:sharing, :blocks] == t[0, :blocks]).all()
+    assert (lens[:sharing] > blocks * 16).all()
+    others = t[sharing:]
+    assert not np.isin(others, t[0, :blocks]).any()
+    check_layout(w)
+
+
+def test_no_group_without_sharing():
+    w = wl.llama3_8b_gqa_bf16()
+    assert (w.sharing_seqs, w.shared_blocks) == (0, 0)
