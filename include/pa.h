@@ -342,6 +342,24 @@ int pa_bm_append_slots(pa_block_manager* bm, const int64_t* seq_ids, int n, int6
 int pa_bm_block_tables(const pa_block_manager* bm, const int64_t* seq_ids, int n, int32_t* tables_out, int max_blocks,
                        int32_t* lens_out);
 
+/*
+ * The shared-prefix groups of a batch, as pa_decode_shared_prefix takes them
+ * ("vLLM 前世今生" §3.2: forked sequences hold their common prompt in the same
+ * physical blocks). seq_ids lists the batch in the order of its block-table
+ * rows (as passed to pa_bm_block_tables). A group is a maximal run of
+ * consecutive listed sequences that each hold at least min_blocks leading
+ * blocks in common with the run's first sequence, counting only blocks that
+ * are full in both; groups_out[3g .. 3g+2] = (index of its first sequence in
+ * seq_ids, number of sequences >= 2, leading blocks shared by all of them).
+ * Runs past max_groups are not reported (their sequences then read their
+ * blocks themselves). *num_groups receives the count written. List forks of
+ * one prompt next to each other to find them. Errors: PA_ERR_NULL,
+ * PA_ERR_SHAPE (min_blocks < 1 or max_groups < 0), PA_ERR_STATE (unknown
+ * sequence); nothing is written on error except *num_groups = 0.
+ */
+int pa_bm_shared_prefix(const pa_block_manager* bm, const int64_t* seq_ids, int n, int min_blocks,
+                        int32_t* groups_out, int max_groups, int* num_groups);
+
 /* Message for the last non-zero status returned on this thread ("" if none). */
 const char* pa_last_error(void);
 

@@ -24,7 +24,7 @@ EXPORTS = ("pa_reshape_and_cache", "pa_decode", "pa_decode_split", "pa_decode_wo
            "pa_decode_shared_prefix", "pa_decode_shared_prefix_workspace_bytes",
            "pa_decode_partition_blocks", "pa_prefill", "pa_copy_blocks", "pa_bm_create", "pa_bm_destroy", "pa_bm_num_free_blocks",
            "pa_bm_block_refcount", "pa_bm_add_sequence", "pa_bm_fork", "pa_bm_free_sequence", "pa_bm_append_slots",
-           "pa_bm_block_tables", "pa_last_error", "pa_version")
+           "pa_bm_block_tables", "pa_bm_shared_prefix", "pa_last_error", "pa_version")
 
 _lock = threading.Lock()
 _lib = None
@@ -87,6 +87,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
         lib.pa_bm_append_slots.restype = _i32
         lib.pa_bm_block_tables.argtypes = [_vp, _vp, _i32, _vp, _i32, _vp]
         lib.pa_bm_block_tables.restype = _i32
+        lib.pa_bm_shared_prefix.argtypes = [_vp, _vp, _i32, _i32, _vp, _i32, ctypes.POINTER(_i32)]
+        lib.pa_bm_shared_prefix.restype = _i32
         lib.pa_last_error.argtypes = []
         lib.pa_last_error.restype = ctypes.c_char_p
         lib.pa_version.argtypes = []
@@ -321,6 +323,16 @@ class BlockManager:
         _check(self._lib, self._lib.pa_bm_block_tables(self._h, ids.ctypes.data, len(ids), tables.ctypes.data, m,
                                                        lens.ctypes.data))
         return tables, lens
+
+    def shared_prefix(self, seq_ids, min_blocks: int = 1, max_groups: int = 16):
+        """Shared-prefix groups of the batch listed in this order: [(first index, count, shared blocks), ...]."""
+        import numpy as np
+        ids = np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int64))
+        out = np.empty((max(max_groups, 1), 3), np.int32)
+        k = _i32(0)
+        _check(self._lib, self._lib.pa_bm_shared_prefix(self._h, ids.ctypes.data, len(ids), min_blocks,
+                                                        out.ctypes.data, max_groups, ctypes.byref(k)))
+        return [tuple(int(x) for x in out[g]) for g in range(k.value)]
 
 
 def prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc, scale: float, num_kv_heads: int,

@@ -13,6 +13,7 @@
 // Data layout: the free list is a stack of block ids; every block has a
 // reference count; every live sequence has its block list and its length.
 // Nothing here touches device memory.
+#include <algorithm>
 #include <cstdint>
 #include <unordered_map>
 #include <vector>
@@ -164,6 +165,53 @@ int pa_bm_block_tables(const pa_block_manager* bm, const int64_t* seq_ids, int n
     int32_t* row = tables_out + (int64_t)i * max_blocks;
     for (int j = 0; j < max_blocks; ++j) row[j] = j < (int)s.blocks.size() ? s.blocks[j] : -1;
     lens_out[i] = (int32_t)s.len;
+  }
+  return pa::ok();
+}
+
+int pa_bm_shared_prefix(const pa_block_manager* bm, const int64_t* seq_ids, int n, int min_blocks,
+                        int32_t* groups_out, int max_groups, int* num_groups) {
+  if (!bm || (n > 0 && !seq_ids) || (max_groups > 0 && !groups_out) || !num_groups)
+    return pa::fail(PA_ERR_NULL, "bm_shared_prefix: NULL argument");
+  if (min_blocks < 1 || max_groups < 0)
+    return pa::fail(PA_ERR_SHAPE, "bm_shared_prefix: min_blocks must be >= 1 and max_groups >= 0");
+  *num_groups = 0;
+  std::vector<const Seq*> list((size_t)(n > 0 ? n : 0));
+  for (int i = 0; i < n; ++i) {
+    auto it = bm->seqs.find(seq_ids[i]);
+    if (it == bm->seqs.end())
+      return pa::fail(PA_ERR_STATE, "bm_shared_prefix: no sequence %lld", (long long)seq_ids[i]);
+    list[(size_t)i] = &it->second;
+  }
+  // Leading blocks two sequences hold in common, counting only blocks full in
+  // both (a shared block is never written again once full, so those stay
+  // shared; a shared partial block is copied before either writes into it).
+  auto common = [&](const Seq& a, const Seq& b) {
+    const int64_t full = std::min(a.len, b.len) / bm->block_size;
+    int64_t j = 0;
+    while (j < full && a.blocks[(size_t)j] == b.blocks[(size_t)j]) ++j;
+    return j;
+  };
+  // A group: a maximal run of consecutive listed sequences that each share at
+  // least min_blocks leading blocks with the run's first; its count of shared
+  // blocks is the smallest of those.
+  for (int i = 0; i < n;) {
+    int end = i + 1;
+    int64_t shared = INT64_MAX;
+    while (end < n) {
+      const int64_t c = common(*list[(size_t)i], *list[(size_t)end]);
+      if (c < min_blocks) break;
+      shared = std::min(shared, c);
+      ++end;
+    }
+    if (end - i >= 2 && *num_groups < max_groups) {
+      int32_t* g = groups_out + 3 * (int64_t)*num_groups;
+      g[0] = i;
+      g[1] = end - i;
+      g[2] = (int32_t)shared;
+      ++*num_groups;
+    }
+    i = end;
   }
   return pa::ok();
 }

@@ -8,6 +8,10 @@ native block manager picks the slots and the copy-on-write pairs; the device
 runs pa_copy_blocks, then pa_reshape_and_cache, then pa_decode over the live
 batch. The oracle replays exactly the same copies, writes and attention on
 the CPU. Both caches must stay byte-identical and every decode must match.
+Each step also lists the batch with the forks of one prompt side by side, asks
+the block manager for the shared-prefix groups of that order
+(pa_bm_shared_prefix) and decodes it through pa_decode_shared_prefix, which
+must give pa_decode's result.
 """
 
 import itertools
@@ -54,6 +58,8 @@ def test_continuous_batching_steps(H, Hkv, D, dtype, cache, path, monkeypatch):
     scale = float(np.float32(1 / np.sqrt(D)))
     ids = itertools.count(1)
     live = []
+    root = {}  # the prompt a sequence descends from
+    grouped = 0
 
     def write(seqs_slots):
         slots = np.asarray(seqs_slots, dtype=np.int64)
@@ -68,12 +74,15 @@ def test_continuous_batching_steps(H, Hkv, D, dtype, cache, path, monkeypatch):
         if len(live) < 10 and (step == 0 or rng.random() < 0.5):
             s = next(ids)
             bm.add_sequence(s)
+            root[s] = s
             prompt = [int(bm.append_slots([s])[0][0]) for _ in range(int(rng.integers(1, 60)))]
             write(prompt)
             live.append(s)
         if live and rng.random() < 0.35:
             child = next(ids)
-            bm.fork(int(rng.choice(live)), child)
+            parent = int(rng.choice(live))
+            bm.fork(parent, child)
+            root[child] = root[parent]
             live.append(child)
             forks += 1
         if len(live) > 3 and rng.random() < 0.25:
@@ -97,12 +106,25 @@ def test_continuous_batching_steps(H, Hkv, D, dtype, cache, path, monkeypatch):
         assert np.isfinite(got).all(), f"step {step}: non-finite output"
         err = float(np.abs(got - ref).max())
         assert err <= TOL[cache], f"step {step}: max|err| = {err}"
+        order = sorted(live, key=lambda s: (root[s], s))
+        groups = bm.shared_prefix(order)
+        if groups:
+            idx = torch.tensor([live.index(s) for s in order])
+            t2, l2 = bm.block_tables(order)
+            out2 = torch.empty_like(out)
+            binding.decode_shared_prefix(out2, q[idx].cuda(), kc_d, vc_d, torch.from_numpy(t2).cuda(),
+                                         torch.from_numpy(l2).cuda(), scale, Hkv, groups, B, kscale, vscale)
+            diff = float((out2 - out[idx.cuda()]).abs().max())
+            assert diff <= 1e-4, f"step {step}: shared-prefix decode differs from pa_decode by {diff} ({groups})"
+            grouped += 1
         if step % 5 == 4:
             torch.cuda.synchronize()
             assert np.array_equal(raw(kc_d.cpu()).view(np.uint8), kc_o.view(np.uint8)), f"step {step}: K cache differs"
             assert np.array_equal(raw(vc_d.cpu()).view(np.uint8), vc_o.view(np.uint8)), f"step {step}: V cache differs"
-    print(f"[batching] done: {forks} forks, {frees} finished, {copies} block copies, {len(live)} live", flush=True)
+    print(f"[batching] done: {forks} forks, {frees} finished, {copies} block copies, {len(live)} live, "
+          f"{grouped} steps with shared-prefix groups", flush=True)
     assert forks and copies, "the run must exercise forking and copy-on-write"
+    assert grouped, "the run must produce shared-prefix groups"
 
 
 @pytest.mark.parametrize("cache", ["f16", "fp8_e4m3"])

@@ -195,3 +195,115 @@ def test_create_rejects_bad_arguments(lib):
         binding.BlockManager(0, 4)
     with pytest.raises(binding.PAError):
         binding.BlockManager(8, 4, block_size=8)
+
+
+def check_groups(bm, order, groups, min_blocks, model=None):
+    """The contract of pa_bm_shared_prefix, checked against the tables (and the token histories)."""
+    tables, lens = bm.block_tables(order) if order else (np.zeros((0, bm.max_blocks_per_seq), np.int32), [])
+    prev_end = 0
+    for first, count, shared in groups:
+        assert first >= prev_end and count >= 2 and first + count <= len(order) and shared >= min_blocks
+        prev_end = first + count
+        for i in range(first, first + count):
+            assert (tables[i, :shared] == tables[first, :shared]).all()  # the decode reads the first row
+            assert lens[i] >= shared * B                                   # and treats those blocks as full
+            if model is not None:  # the same tokens, not only the same block ids
+                assert model.history[order[i]][:shared * B] == model.history[order[first]][:shared * B]
+        # maximal: the next listed sequence does not share min_blocks full leading blocks with the first
+        if prev_end < len(order):
+            full = min(lens[first], lens[prev_end]) // B
+            same = 0
+            while same < full and tables[prev_end, same] == tables[first, same]:
+                same += 1
+            assert same < min_blocks
+
+
+def test_shared_prefix_groups_of_forks(lib):
+    bm = binding.BlockManager(64, max_blocks_per_seq=16)
+    m = Model(64)
+    for s in (1, 9):
+        bm.add_sequence(s)
+        m.history[s] = []
+    for _ in range(100):
+        append(bm, m, [1])            # A: 100 tokens, 6 full blocks + 4 tokens in the 7th
+    for _ in range(40):
+        append(bm, m, [9])            # D: unrelated
+    for c in (2, 3):
+        bm.fork(1, c)
+        m.history[c] = list(m.history[1])
+    assert bm.shared_prefix([1, 2, 3, 9]) == [(0, 3, 6)]  # the shared partial 7th block is not counted
+    append(bm, m, [1, 2, 3])          # two of them copy the 7th block; the 6 full blocks stay shared
+    m.check(bm)
+    assert bm.shared_prefix([1, 2, 3, 9]) == [(0, 3, 6)]
+    assert bm.shared_prefix([9, 1, 2, 3]) == [(1, 3, 6)]
+    assert bm.shared_prefix([1, 9, 2, 3]) == [(2, 2, 6)]  # a sequence in between ends the run
+    assert bm.shared_prefix([1, 2, 3, 9], min_blocks=7) == []
+    assert bm.shared_prefix([1, 2, 3, 9], max_groups=0) == []
+    # nested forks: B grows past the fork, C forks from B; B and C share more than A does with either
+    for _ in range(40):
+        append(bm, m, [2])            # B: 141 tokens, its own blocks from the 7th on
+    bm.fork(2, 4)
+    m.history[4] = list(m.history[2])
+    assert bm.shared_prefix([2, 4]) == [(0, 2, 8)]      # 8 full blocks in common (the 9th is partial)
+    assert bm.shared_prefix([2, 4, 1, 3]) == [(0, 4, 6)]  # the run's count is its smallest
+    for order in ([1, 2, 3, 4, 9], [2, 4, 1, 3, 9], [9, 4, 2]):
+        for mb in (1, 6, 7):
+            check_groups(bm, order, bm.shared_prefix(order, min_blocks=mb), mb, m)
+
+
+def test_shared_prefix_errors(lib):
+    bm = binding.BlockManager(8, max_blocks_per_seq=4)
+    bm.add_sequence(1)
+    with pytest.raises(binding.PAError) as e:
+        bm.shared_prefix([1, 5])
+    assert e.value.code == 8
+    with pytest.raises(binding.PAError) as e:
+        bm.shared_prefix([1], min_blocks=0)
+    assert e.value.code == 3
+    assert bm.shared_prefix([]) == [] and bm.shared_prefix([1]) == []
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_shared_prefix_groups_in_random_workloads(lib, seed):
+    # The random add / fork / append / free workload; after every step the live batch, listed by id and
+    # listed by first block (which puts forks of one prompt together), gives groups that keep the contract.
+    rng = np.random.default_rng(100 + seed)
+    N, M = 96, 12
+    bm = binding.BlockManager(N, max_blocks_per_seq=M)
+    m = Model(N)
+    new_id = itertools.count(100)
+    found = 0
+    for step in range(200):
+        live = sorted(m.history)
+        op = rng.random()
+        if op < 0.15 or not live:
+            s = next(new_id)
+            bm.add_sequence(s)
+            m.history[s] = []
+        elif op < 0.3:
+            parent = int(rng.choice(live))
+            child = next(new_id)
+            bm.fork(parent, child)
+            m.history[child] = list(m.history[parent])
+        elif op < 0.38:
+            s = int(rng.choice(live))
+            bm.free_sequence(s)
+            del m.history[s]
+        else:
+            seqs = [int(x) for x in rng.choice(live, size=int(rng.integers(1, len(live) + 1)), replace=False)]
+            try:
+                append(bm, m, seqs)
+            except binding.PAError as e:
+                assert e.code == 7
+                victim = int(rng.choice(live))
+                bm.free_sequence(victim)
+                del m.history[victim]
+        live = sorted(m.history)
+        tables, _ = bm.block_tables(live) if live else (np.zeros((0, M), np.int32), None)
+        by_first = [s for _, s in sorted(zip(tables[:, 0].tolist(), live))] if live else []
+        for order in (live, by_first):
+            for mb in (1, 2):
+                groups = bm.shared_prefix(order, min_blocks=mb)
+                check_groups(bm, order, groups, mb, m)
+                found += len(groups)
+    assert found > 0, "the workload never produced a shared prefix"
