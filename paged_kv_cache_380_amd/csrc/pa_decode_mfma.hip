@@ -12,7 +12,7 @@
 // which leaves the kernel ALU-bound below the HBM roofline; here they are
 // issued as MFMA instructions, and the vector ALU only runs the online softmax.
 //
-// Two schedules share the per-block arithmetic below:
+// Three modes share the per-block arithmetic below:
 //  * partitioned: one workgroup of 4 waves per (sequence, KV head, head tile
 //    of GT <= 16, partition), wave w taking blocks w, w+4, ... of the
 //    partition, with the block-table slice staged in LDS; the waves merge
@@ -23,7 +23,16 @@
 //    sequence inside the range) and leaves each piece's partial result for
 //    decode_bal_reduce, or writes a sequence it holds whole. GT may be 32
 //    here: two 16-head sub-tiles per wave share every K/V block it loads.
-// In both, a wave keeps the next blocks' K/V loads in flight while it works.
+//    With the shared-prefix pass (a.shared_prefix) each sequence's first
+//    ws_shared[s] blocks are left out of the ranges: that pass read them.
+//  * shared-prefix pass (kPrefix, GT = 16): the 16 columns of a tile are the
+//    (sequence, head) pairs of 16 / group consecutive sequences of one group
+//    that share their first blocks ("vLLM 前世今生" §3.2: a common prompt in
+//    the same physical blocks), so every shared K/V tile is read and
+//    multiplied once for all of them; workgroups are (KV head, part of
+//    kPrefixPartBlocks shared blocks, tile) and leave per-part partial
+//    results for decode_bal_reduce.
+// In all, a wave keeps the next blocks' K/V loads in flight while it works.
 //
 //  * K is loaded straight from HBM in the MFMA A-operand layout: lane l reads
 //    16 bytes of token l % 16 (64 contiguous bytes per token per instruction),
