@@ -244,7 +244,7 @@ def main():
         return
 
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path.",
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this library has no multi-GPU path.",
               file=sys.stderr)
         sys.exit(2)
 
