@@ -81,7 +81,8 @@ def sharing(name, H, Hkv, D, dtype, cache, shared, tails, private, seed, kv_scal
 
 
 @pytest.mark.parametrize("H,Hkv,dtype,cache", [(32, 8, "bf16", "fp8_e4m3"), (32, 8, "bf16", "bf16"),
-                                               (16, 2, "f16", "f16"), (16, 1, "bf16", "bf16")])
+                                               (16, 2, "f16", "f16"), (16, 1, "bf16", "bf16"),
+                                               (16, 2, "f16", "fp8_e4m3"), (16, 1, "bf16", "fp8_e4m3")])
 def test_group_in_the_middle(H, Hkv, dtype, cache):
     # 7 sharing sequences (not a multiple of 4 or 2) between private ones; 75 shared blocks (2 parts, the
     # second of 11 blocks); tails from one token to several ranges
@@ -109,6 +110,15 @@ def test_single_sequence_groups():
     w = wl.build("shared_single", [64, 64 + 3, 48, 16 * 70 + 9, 16 * 70 + 9, 200], 32, 8, 128, "bf16", seed=23,
                  free_fraction=0.1)
     check(w, [(0, 1, 4), (1, 1, 4), (2, 1, 3), (3, 1, 70), (4, 1, 5)])
+
+
+@pytest.mark.parametrize("cache", ["fp8_e4m3", "f16"])
+def test_head_size_64_other_caches(cache):
+    rng = np.random.default_rng(17)
+    dtype = "f16" if cache == "f16" else "bf16"
+    w = sharing("shared_d64_" + cache, 32, 8, 64, dtype, cache, 40, [int(rng.integers(1, 700)) for _ in range(13)],
+                [int(rng.integers(1, 900)) for _ in range(5)], seed=29)
+    check(reorder(w, list(range(13, 15)) + list(range(13)) + list(range(15, 18))), [(2, 13, 40)])
 
 
 def test_head_size_64_and_native_output():
