@@ -302,9 +302,19 @@ def main():
             binding.decode(out, case.q, case.kc, case.vc, case.tables, case.lens, w.scale, w.num_kv_heads,
                            w.block_size, w.k_scale, w.v_scale, partition_blocks=args.partition_blocks, workspace=ws)
 
+    # The step: append the newest token of every sequence, then attend. pa_decode_append does both (one launch
+    # where the decode kernel writes the rows itself); with the shared-prefix pass or an explicit partition
+    # length the append is its own pa_reshape_and_cache launch.
+    one_call = not prefix and args.partition_blocks == 0
+
     def step():
-        case.append()
-        run_decode()
+        if one_call:
+            binding.decode_append(out, case.q, case.new_key, case.new_value, case.kc, case.vc, case.new_slots,
+                                  case.tables, case.lens, w.scale, w.num_kv_heads, w.block_size, w.k_scale,
+                                  w.v_scale, workspace=ws)
+        else:
+            case.append()
+            run_decode()
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -376,6 +386,7 @@ def main():
             "schedule": "balanced" if balanced_schedule(w, args.partition_blocks) else f"partitions of {pb} blocks",
             "decode_path": os.environ.get("PA_DECODE_PATH", "auto"),
             "shared_prefix": [0, w.sharing_seqs, w.shared_blocks] if prefix else None,
+            "append": ("in the decode kernel" if one_call and append_fuses(w) else "reshape_and_cache kernel"),
         },
         "pct_of_hbm_peak": round(100 * kv_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
         "seq_steps_per_s": round(w.num_seqs / (ms_per_step * 1e-3), 1),
@@ -508,6 +519,14 @@ def balanced_schedule(w, partition_blocks: int) -> bool:
     """Whether the library picks its balanced schedule here (its selection rule, restated)."""
     return (decode_kernel(w) == "decode_mfma" and partition_blocks == 0 and w.num_seqs <= 1024
             and w.num_seqs * w.max_blocks_per_seq <= 2**31 - 1)
+
+
+def append_fuses(w) -> bool:
+    """Whether pa_decode_append writes the new rows inside the decode kernel (the library's rule, restated):
+    the vector-ALU kernel with one workgroup per KV head."""
+    group = w.num_heads // w.num_kv_heads
+    tile = next(t for t in (8, 4, 2, 1) if group % t == 0)
+    return decode_kernel(w) == "decode_main" and tile == group
 
 
 def shared_prefix_applies(w, partition_blocks: int) -> bool:

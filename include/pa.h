@@ -270,6 +270,36 @@ int pa_decode_shared_prefix(void* out, const void* q, const void* k_cache, const
 size_t pa_decode_shared_prefix_workspace_bytes(int num_seqs, int num_heads, int num_kv_heads, int head_size,
                                                int max_blocks_per_seq, int block_size, int max_shared_blocks);
 
+/*
+ * pa_decode_append -- one whole decode step: the newest token of every
+ * sequence is written into its cache slot, then every sequence attends over
+ * its context (the order "vLLM 前世今生" §3.2-3.3 implies for a step: the
+ * cache holds the new token's K/V before attention reads it). Same result as
+ * pa_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, ...,
+ * num_tokens = num_seqs) followed by pa_decode(...).
+ *
+ *   key, value      device, [num_seqs, num_kv_heads, head_size], q_dtype: the new
+ *                   token of sequence s is row s
+ *   slot_mapping    device, [num_seqs]; int64 if slot_is_int64 else int32; a
+ *                   negative slot writes nothing. Each slot must lie in a block
+ *                   that only its own sequence reads in this batch (the last,
+ *                   private block, as after copy-on-write).
+ *   others          as in pa_decode (k_cache, v_cache written as by
+ *                   pa_reshape_and_cache; k_scale / v_scale also encode FP8)
+ *
+ * Where the vector-ALU kernel runs with one workgroup per (sequence, KV head)
+ * -- MHA or two query heads per KV head with F16/BF16 queries, 1, 2, 4 or 8
+ * with F32 queries -- that workgroup writes its KV head's new row before it
+ * reads the block (one launch instead of two). Elsewhere the reshape kernel
+ * runs first. Errors as in pa_reshape_and_cache and pa_decode.
+ */
+int pa_decode_append(void* out, const void* q, const void* key, const void* value, void* k_cache, void* v_cache,
+                     const void* slot_mapping, int slot_is_int64, const int32_t* block_tables,
+                     const int32_t* context_lens, float scale, int num_kv_heads, int block_size, int num_seqs,
+                     int num_heads, int head_size, int max_blocks_per_seq, int64_t num_blocks, pa_dtype q_dtype,
+                     pa_dtype cache_dtype, pa_dtype out_dtype, float k_scale, float v_scale, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
 /* Partition length (in blocks) pa_decode would choose for these shapes. */
 int pa_decode_partition_blocks(int num_seqs, int num_heads, int num_kv_heads, int head_size,
                                int max_blocks_per_seq, int block_size);

@@ -21,7 +21,7 @@ STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_DTYPE", 3: "PA_ERR_SHAPE", 4:
           5: "PA_ERR_WORKSPACE", 6: "PA_ERR_LAUNCH", 7: "PA_ERR_CAPACITY", 8: "PA_ERR_STATE"}
 
 EXPORTS = ("pa_reshape_and_cache", "pa_decode", "pa_decode_split", "pa_decode_workspace_bytes",
-           "pa_decode_shared_prefix", "pa_decode_shared_prefix_workspace_bytes",
+           "pa_decode_shared_prefix", "pa_decode_shared_prefix_workspace_bytes", "pa_decode_append",
            "pa_decode_partition_blocks", "pa_prefill", "pa_copy_blocks", "pa_bm_create", "pa_bm_destroy", "pa_bm_num_free_blocks",
            "pa_bm_block_refcount", "pa_bm_add_sequence", "pa_bm_fork", "pa_bm_free_sequence", "pa_bm_append_slots",
            "pa_bm_block_tables", "pa_bm_shared_prefix", "pa_last_error", "pa_version")
@@ -59,6 +59,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
         lib.pa_decode_split.restype = _i32
         lib.pa_decode_shared_prefix.argtypes = dec + [_vp, _i32, _vp, _sz, _vp]
         lib.pa_decode_shared_prefix.restype = _i32
+        lib.pa_decode_append.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _f32, _i32, _i32, _i32,
+                                         _i32, _i32, _i32, _i64, _i32, _i32, _i32, _f32, _f32, _vp, _sz, _vp]
+        lib.pa_decode_append.restype = _i32
         lib.pa_decode_shared_prefix_workspace_bytes.argtypes = [_i32] * 7
         lib.pa_decode_shared_prefix_workspace_bytes.restype = _sz
         lib.pa_decode_workspace_bytes.argtypes = [_i32] * 7
@@ -244,6 +247,39 @@ def decode_shared_prefix(out, q, k_cache, v_cache, block_tables, context_lens, s
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens), float(scale),
         num_kv_heads, block_size, S, H, D, M, N, _dtype(q), _dtype(k_cache), _dtype(out), float(k_scale),
         float(v_scale), ctypes.cast(flat, _vp), len(groups), ws_ptr, ws_bytes, _stream(q, stream)))
+    return out
+
+
+def decode_append(out, q, key, value, k_cache, v_cache, slot_mapping, block_tables, context_lens, scale: float,
+                  num_kv_heads: int, block_size: int = 16, k_scale: float = 1.0, v_scale: float = 1.0,
+                  workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """A whole decode step: write row s of key/value [S, Hkv, D] into slot_mapping[s] (int32 or int64), then
+    decode. Same result as :func:`reshape_and_cache` followed by :func:`decode`."""
+    lib = load()
+    for t in (out, q, key, value, k_cache, v_cache, slot_mapping, block_tables, context_lens):
+        _need(t.is_cuda and t.is_contiguous(), "all tensors must be contiguous device tensors")
+    _need(q.dim() == 3 and out.shape == q.shape, "q/out must be [S, H, D] of one shape")
+    S, H, D = q.shape
+    _need(k_cache.dim() == 4 and v_cache.shape == k_cache.shape and k_cache.dtype == v_cache.dtype,
+          "caches must be [N, Hkv, B, D] of one shape and dtype")
+    N, Hkv, B, D2 = k_cache.shape
+    _need(Hkv == num_kv_heads and B == block_size and D2 == D, "cache shape does not match the arguments")
+    _need(key.shape == (S, Hkv, D) and value.shape == key.shape and key.dtype == q.dtype and value.dtype == q.dtype,
+          "key/value must be [S, Hkv, D] in the query dtype")
+    _need(slot_mapping.dtype in (torch.int32, torch.int64) and slot_mapping.shape == (S,),
+          "slot_mapping must be int32 or int64 [S]")
+    _need(block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32 and block_tables.dim() == 2
+          and block_tables.shape[0] == S and context_lens.shape == (S,), "block_tables [S, M] and context_lens [S] int32")
+    M = block_tables.shape[1]
+    if workspace is None:
+        workspace = workspace_for(q, num_kv_heads, block_tables, 0, block_size)
+    ws_ptr = _ptr(workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib, lib.pa_decode_append(
+        _ptr(out), _ptr(q), _ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping),
+        1 if slot_mapping.dtype == torch.int64 else 0, _ptr(block_tables), _ptr(context_lens), float(scale),
+        num_kv_heads, block_size, S, H, D, M, N, _dtype(q), _dtype(k_cache), _dtype(out), float(k_scale),
+        float(v_scale), ws_ptr, ws_bytes, _stream(q, stream)))
     return out
 
 

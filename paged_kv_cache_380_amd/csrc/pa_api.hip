@@ -300,13 +300,25 @@ size_t pa_decode_workspace_bytes(int num_seqs, int num_heads, int num_kv_heads, 
 
 namespace {
 
-// pa_decode_split and pa_decode_shared_prefix: validation, schedule choice, launch.
-// groups (host, [num_groups][3]) name the shared-prefix groups, or are NULL.
+// The new tokens of pa_decode_append (one per sequence), for the fused path.
+struct Append {
+  const void* key;
+  const void* value;
+  const void* slots;
+  int slots_int64;
+};
+
+// pa_decode_split, pa_decode_shared_prefix and pa_decode_append: validation,
+// schedule choice, launch. groups (host, [num_groups][3]) name the
+// shared-prefix groups, or are NULL; app, when set, asks the decode kernel to
+// write the new tokens first (the caller has checked that the vector-ALU
+// kernel with one workgroup per KV head runs).
 int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
                 const int32_t* context_lens, float scale, int num_kv_heads, int block_size, int num_seqs,
                 int num_heads, int head_size, int max_blocks_per_seq, int64_t num_blocks, pa_dtype q_dtype,
                 pa_dtype cache_dtype, pa_dtype out_dtype, float k_scale, float v_scale, int partition_blocks,
-                const int32_t* groups, int num_groups, void* workspace, size_t workspace_bytes, void* stream) {
+                const int32_t* groups, int num_groups, void* workspace, size_t workspace_bytes, void* stream,
+                const Append* app = nullptr) {
   if (block_size != 16) return fail(PA_ERR_UNSUPPORTED, "decode: block_size must be 16 (got %d)", block_size);
   if (head_size != 64 && head_size != 128)
     return fail(PA_ERR_UNSUPPORTED, "decode: head_size must be 64 or 128 (got %d)", head_size);
@@ -432,6 +444,15 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
     a.grp_tile0[num_groups] = tiles;
     if (prefix_parts > 65535) return fail(PA_ERR_UNSUPPORTED, "decode: shared prefix too long");
   }
+  if (app) {
+    a.append = 1;
+    a.new_key = app->key;
+    a.new_value = app->value;
+    a.new_slots = app->slots;
+    a.new_slots_int64 = app->slots_int64;
+    a.enc_k_scale = k_scale;
+    a.enc_v_scale = v_scale;
+  }
   const hipError_t e = pa::launch_decode(a, q_dtype, cache_dtype, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "decode: launch failed: %s", hipGetErrorString(e));
   return ok();
@@ -478,6 +499,42 @@ size_t pa_decode_shared_prefix_workspace_bytes(int num_seqs, int num_heads, int 
                                      balanced_ranges(num_heads, balanced_tile(num_heads / num_kv_heads), true)).total;
   const size_t total = prefix_layout(bal, num_seqs, num_heads, head_size, prefix_parts_for(max_shared_blocks)).total;
   return total > base ? total : base;
+}
+
+int pa_decode_append(void* out, const void* q, const void* key, const void* value, void* k_cache, void* v_cache,
+                     const void* slot_mapping, int slot_is_int64, const int32_t* block_tables,
+                     const int32_t* context_lens, float scale, int num_kv_heads, int block_size, int num_seqs,
+                     int num_heads, int head_size, int max_blocks_per_seq, int64_t num_blocks, pa_dtype q_dtype,
+                     pa_dtype cache_dtype, pa_dtype out_dtype, float k_scale, float v_scale, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  // The decode kernel can write the new rows itself where it runs the vector-ALU
+  // kernel with one workgroup per (sequence, KV head, partition): only that
+  // workgroup then reads the block holding the new row for its KV head. That is
+  // MHA or two query heads per KV head with 16-bit queries, and groups of 1, 2,
+  // 4 or 8 with float32 queries. Elsewhere the rows are written by the reshape
+  // kernel first (two launches, same result).
+  const int group = num_kv_heads >= 1 && num_heads % num_kv_heads == 0 ? num_heads / num_kv_heads : 0;
+  const bool sixteen = q_dtype == PA_DTYPE_F16 || q_dtype == PA_DTYPE_BF16;
+  const bool fused = group > 0 && !use_mfma(q_dtype, group) && pa::group_tile_for(group) == group &&
+                     !(group >= 4 && sixteen);
+  if (num_seqs > 0 && (!key || !value || !slot_mapping))
+    return fail(PA_ERR_NULL, "decode_append: NULL key, value or slot_mapping");
+  if (!fused) {
+    const int rc = pa_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, slot_is_int64, num_seqs,
+                                        num_kv_heads, head_size, num_blocks, block_size, q_dtype, cache_dtype,
+                                        k_scale, v_scale, stream);
+    if (rc != PA_OK) return rc;
+    return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, scale, num_kv_heads, block_size,
+                       num_seqs, num_heads, head_size, max_blocks_per_seq, num_blocks, q_dtype, cache_dtype,
+                       out_dtype, k_scale, v_scale, 0, nullptr, 0, workspace, workspace_bytes, stream);
+  }
+  if (cache_dtype == PA_DTYPE_FP8_E4M3 &&
+      !(std::isfinite(k_scale) && std::isfinite(v_scale) && k_scale > 0.f && v_scale > 0.f))
+    return fail(PA_ERR_SHAPE, "decode_append: FP8 scales must be finite and positive");
+  const Append app{key, value, slot_mapping, slot_is_int64 ? 1 : 0};
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, scale, num_kv_heads, block_size, num_seqs,
+                     num_heads, head_size, max_blocks_per_seq, num_blocks, q_dtype, cache_dtype, out_dtype, k_scale,
+                     v_scale, 0, nullptr, 0, workspace, workspace_bytes, stream, &app);
 }
 
 int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,

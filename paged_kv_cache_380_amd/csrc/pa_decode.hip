@@ -163,6 +163,37 @@ __device__ __forceinline__ float swap_sum16(float a, float b) {
 constexpr int kDppRowRor8 = 0x128;  // lane j <- lane (j - 8) mod 16, i.e. j ^ 8
 constexpr int kDppRowRor4 = 0x124;  // lane j <- lane (j - 4) mod 16
 
+// Fused append: write sequence seq's new K and V rows of KV head kvh into the
+// cache slot a.new_slots[seq] (bit copy, or E4M3 after dividing by the scale,
+// exactly as reshape_kernel does), one 16-byte source chunk per thread. The
+// workgroup's next barrier makes the rows visible to its other waves, which
+// are the only readers of that block for this KV head in the launch.
+template <int QK, int CK, int D>
+__device__ __forceinline__ void append_row(const DecodeArgs& a, int seq, int kvh, int tid) {
+  const int64_t slot = a.new_slots_int64 ? static_cast<const int64_t*>(a.new_slots)[seq]
+                                         : (int64_t) static_cast<const int32_t*>(a.new_slots)[seq];
+  if (slot < 0 || slot >= a.num_blocks * 16) return;
+  constexpr int kSrc = KindBytes<QK>::value;
+  constexpr int E = 16 / kSrc;  // source elements per chunk
+  constexpr int NC = D / E;     // chunks per row
+  const int64_t src = ((int64_t)seq * a.num_kv_heads + kvh) * D;
+  const int64_t dst = (((slot >> 4) * a.num_kv_heads + kvh) * 16 + (slot & 15)) * D;
+  for (int i = tid; i < 2 * NC; i += kThreads) {
+    const bool is_v = i >= NC;
+    const int c = is_v ? i - NC : i;
+    const uint4 x = *reinterpret_cast<const uint4*>(static_cast<const char*>(is_v ? a.new_value : a.new_key) +
+                                                     (src + (int64_t)c * E) * kSrc);
+    char* cache = static_cast<char*>(const_cast<void*>(is_v ? a.v_cache : a.k_cache));
+    if constexpr (CK == QK) {
+      *reinterpret_cast<uint4*>(cache + (dst + (int64_t)c * E) * kSrc) = x;
+    } else if constexpr (CK == kFP8 && QK == kF32) {
+      *reinterpret_cast<uint32_t*>(cache + dst + (int64_t)c * E) = e4m3_chunk32(x, is_v ? a.enc_v_scale : a.enc_k_scale);
+    } else if constexpr (CK == kFP8) {
+      *reinterpret_cast<uint2*>(cache + dst + (int64_t)c * E) = e4m3_chunk16<QK>(x, is_v ? a.enc_v_scale : a.enc_k_scale);
+    }
+  }
+}
+
 template <int QK, int CK, int D, int GT>
 __global__ __launch_bounds__(kThreads) void decode_main(const DecodeArgs a) {
   using Geo = TileGeo<CK, D>;
@@ -186,6 +217,11 @@ __global__ __launch_bounds__(kThreads) void decode_main(const DecodeArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   const int ctx = context_len(a, seq);
+  // Fused append: by the one workgroup that reads the sequence's last block
+  // for this KV head (the launch has one workgroup per KV head), before it
+  // stages anything; an empty context's row goes out with partition 0.
+  if (a.append && part == (ctx > 0 ? (((ctx + 15) >> 4) - 1) / a.partition_blocks : 0))
+    append_row<QK, CK, D>(a, seq, kvh, tid);
   if (ctx <= 0) {  // nothing to attend
     write_zeros<GT, D>(a, seq, h0, part, tid);
     return;

@@ -75,6 +75,39 @@ __device__ __forceinline__ uint32_t e4m3_encode(float y) {
   return sign | ((r >> 20) - (120u << 3));
 }
 
+// x / scale rounded once (float32 division of |x|, the sign put back, so a NaN keeps its sign).
+__device__ __forceinline__ float e4m3_quotient(float x, float scale) { return __builtin_copysignf(__builtin_fabsf(x) / scale, x); }
+
+// Eight 16-bit source elements -> eight E4M3 bytes.
+// The 8 16-bit values of a 16-byte chunk (SRC = kF16 or kBF16) as 8 E4M3 codes.
+template <int SRC>
+__device__ __forceinline__ uint2 e4m3_chunk16(const uint4& v, float scale) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t o[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float lo, hi;
+    if constexpr (SRC == kBF16) {
+      lo = bf16_lo(w[i]);
+      hi = bf16_hi(w[i]);
+    } else {
+      lo = f16_lo(w[i]);
+      hi = f16_hi(w[i]);
+    }
+    const uint32_t b = e4m3_encode(e4m3_quotient(lo, scale)) | (e4m3_encode(e4m3_quotient(hi, scale)) << 8);
+    o[i >> 1] |= b << ((i & 1) * 16);
+  }
+  return make_uint2(o[0], o[1]);
+}
+
+// Four float32 source elements -> four E4M3 bytes.
+// The 4 float32 values of a 16-byte chunk as 4 E4M3 codes.
+__device__ __forceinline__ uint32_t e4m3_chunk32(const uint4& v, float scale) {
+  return e4m3_encode(e4m3_quotient(__uint_as_float(v.x), scale)) | (e4m3_encode(e4m3_quotient(__uint_as_float(v.y), scale)) << 8) |
+         (e4m3_encode(e4m3_quotient(__uint_as_float(v.z), scale)) << 16) |
+         (e4m3_encode(e4m3_quotient(__uint_as_float(v.w), scale)) << 24);
+}
+
 // Wave-level sum over groups of N consecutive lanes (N = 4, 8, 16 or 32);
 // every lane of a group ends with the same value.
 template <int Ctrl> __device__ __forceinline__ float dpp(float x) {

@@ -16,36 +16,6 @@ constexpr int kThreads = 256;
 
 // x / scale for scale > 0, computed as |x| / scale (one correctly rounded
 // float32 division) with x's sign bit put back, so that a NaN keeps its sign.
-__device__ __forceinline__ float quotient(float x, float scale) { return __builtin_copysignf(__builtin_fabsf(x) / scale, x); }
-
-// Eight 16-bit source elements -> eight E4M3 bytes.
-template <int SRC>
-__device__ __forceinline__ uint2 quant_chunk16(const uint4& v, float scale) {
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  uint32_t o[2] = {0u, 0u};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float lo, hi;
-    if constexpr (SRC == kBF16) {
-      lo = bf16_lo(w[i]);
-      hi = bf16_hi(w[i]);
-    } else {
-      lo = f16_lo(w[i]);
-      hi = f16_hi(w[i]);
-    }
-    const uint32_t b = e4m3_encode(quotient(lo, scale)) | (e4m3_encode(quotient(hi, scale)) << 8);
-    o[i >> 1] |= b << ((i & 1) * 16);
-  }
-  return make_uint2(o[0], o[1]);
-}
-
-// Four float32 source elements -> four E4M3 bytes.
-__device__ __forceinline__ uint32_t quant_chunk32(const uint4& v, float scale) {
-  return e4m3_encode(quotient(__uint_as_float(v.x), scale)) | (e4m3_encode(quotient(__uint_as_float(v.y), scale)) << 8) |
-         (e4m3_encode(quotient(__uint_as_float(v.z), scale)) << 16) |
-         (e4m3_encode(quotient(__uint_as_float(v.w), scale)) << 24);
-}
-
 template <int SRC, int CACHE>
 __global__ __launch_bounds__(kThreads) void reshape_kernel(ReshapeArgs a) {
   constexpr int kSrcBytes = KindBytes<SRC>::value;
@@ -75,11 +45,11 @@ __global__ __launch_bounds__(kThreads) void reshape_kernel(ReshapeArgs a) {
     *reinterpret_cast<uint4*>(static_cast<char*>(a.k_cache) + dst_elem * kSrcBytes) = kv;
     *reinterpret_cast<uint4*>(static_cast<char*>(a.v_cache) + dst_elem * kSrcBytes) = vv;
   } else if constexpr (SRC == kF32) {
-    *reinterpret_cast<uint32_t*>(static_cast<char*>(a.k_cache) + dst_elem) = quant_chunk32(kv, a.k_scale);
-    *reinterpret_cast<uint32_t*>(static_cast<char*>(a.v_cache) + dst_elem) = quant_chunk32(vv, a.v_scale);
+    *reinterpret_cast<uint32_t*>(static_cast<char*>(a.k_cache) + dst_elem) = e4m3_chunk32(kv, a.k_scale);
+    *reinterpret_cast<uint32_t*>(static_cast<char*>(a.v_cache) + dst_elem) = e4m3_chunk32(vv, a.v_scale);
   } else {
-    *reinterpret_cast<uint2*>(static_cast<char*>(a.k_cache) + dst_elem) = quant_chunk16<SRC>(kv, a.k_scale);
-    *reinterpret_cast<uint2*>(static_cast<char*>(a.v_cache) + dst_elem) = quant_chunk16<SRC>(vv, a.v_scale);
+    *reinterpret_cast<uint2*>(static_cast<char*>(a.k_cache) + dst_elem) = e4m3_chunk16<SRC>(kv, a.k_scale);
+    *reinterpret_cast<uint2*>(static_cast<char*>(a.v_cache) + dst_elem) = e4m3_chunk16<SRC>(vv, a.v_scale);
   }
 }
 
