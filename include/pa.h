@@ -281,9 +281,10 @@ size_t pa_decode_shared_prefix_workspace_bytes(int num_seqs, int num_heads, int 
  *   key, value      device, [num_seqs, num_kv_heads, head_size], q_dtype: the new
  *                   token of sequence s is row s
  *   slot_mapping    device, [num_seqs]; int64 if slot_is_int64 else int32; a
- *                   negative slot writes nothing. Each slot must lie in a block
- *                   that only its own sequence reads in this batch (the last,
- *                   private block, as after copy-on-write).
+ *                   negative slot writes nothing. Slot s must be the slot of
+ *                   position context_lens[s] - 1 of sequence s (a decode step's
+ *                   new token), in a block no other sequence of the batch reads
+ *                   (its private last block, as after copy-on-write).
  *   others          as in pa_decode (k_cache, v_cache written as by
  *                   pa_reshape_and_cache; k_scale / v_scale also encode FP8)
  *

@@ -165,10 +165,9 @@ constexpr int kDppRowRor4 = 0x124;  // lane j <- lane (j - 4) mod 16
 
 // Fused append: write sequence seq's new K and V rows of KV head kvh into the
 // cache slot a.new_slots[seq] (bit copy, or E4M3 after dividing by the scale,
-// exactly as reshape_kernel does), one 16-byte source chunk per thread. The
-// workgroup's next barrier makes the rows visible to its other waves, which
-// are the only readers of that block for this KV head in the launch.
-template <int QK, int CK, int D>
+// exactly as reshape_kernel does), one 16-byte source chunk per thread of
+// the N taking part (thread index tid).
+template <int QK, int CK, int D, int N>
 __device__ __forceinline__ void append_row(const DecodeArgs& a, int seq, int kvh, int tid) {
   const int64_t slot = a.new_slots_int64 ? static_cast<const int64_t*>(a.new_slots)[seq]
                                          : (int64_t) static_cast<const int32_t*>(a.new_slots)[seq];
@@ -178,7 +177,7 @@ __device__ __forceinline__ void append_row(const DecodeArgs& a, int seq, int kvh
   constexpr int NC = D / E;     // chunks per row
   const int64_t src = ((int64_t)seq * a.num_kv_heads + kvh) * D;
   const int64_t dst = (((slot >> 4) * a.num_kv_heads + kvh) * 16 + (slot & 15)) * D;
-  for (int i = tid; i < 2 * NC; i += kThreads) {
+  for (int i = tid; i < 2 * NC; i += N) {
     const bool is_v = i >= NC;
     const int c = is_v ? i - NC : i;
     const uint4 x = *reinterpret_cast<const uint4*>(static_cast<const char*>(is_v ? a.new_value : a.new_key) +
@@ -217,12 +216,16 @@ __global__ __launch_bounds__(kThreads) void decode_main(const DecodeArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   const int ctx = context_len(a, seq);
-  // Fused append: by the one workgroup that reads the sequence's last block
-  // for this KV head (the launch has one workgroup per KV head), before it
-  // stages anything; an empty context's row goes out with partition 0.
-  if (a.append && part == (ctx > 0 ? (((ctx + 15) >> 4) - 1) / a.partition_blocks : 0))
-    append_row<QK, CK, D>(a, seq, kvh, tid);
+  // Fused append: the new row (position ctx - 1) lies in the sequence's last
+  // block, which for this KV head only one wave of the launch reads (one
+  // workgroup per KV head; the last partition's wave (nblk - 1) % kWaves, at
+  // the end of its stream). That wave writes the row first; its own later
+  // load of the block sees the stores (wavefront-scope release / acquire),
+  // and the other waves start streaming at once. An empty context's row goes
+  // out with partition 0.
+  const bool writer = a.append && part == (ctx > 0 ? (((ctx + 15) >> 4) - 1) / a.partition_blocks : 0);
   if (ctx <= 0) {  // nothing to attend
+    if (writer) append_row<QK, CK, D, kThreads>(a, seq, kvh, tid);
     write_zeros<GT, D>(a, seq, h0, part, tid);
     return;
   }
@@ -254,6 +257,12 @@ __global__ __launch_bounds__(kThreads) void decode_main(const DecodeArgs a) {
     }
   }
   __syncthreads();
+  // (After the barrier, so that only the writing wave waits for its stores.)
+  if (writer && wave == (nblk - 1) % kWaves) {
+    append_row<QK, CK, D, 64>(a, seq, kvh, lane);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
 
   float m[GT], l[GT], acc[GT][E];
 #pragma unroll
