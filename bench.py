@@ -199,12 +199,25 @@ def cpu_baseline(w, target_seconds: float):
     r1 = resource.getrusage(resource.RUSAGE_SELF)
     cpu = (r1.ru_utime - r0.ru_utime) + (r1.ru_stime - r0.ru_stime)
     del kc, vc
+    try:
+        from threadpoolctl import threadpool_info
+        blas = sorted({(i.get("internal_api"), i.get("num_threads")) for i in threadpool_info()
+                       if i.get("user_api") == "blas"})
+        blas_threads = max((n for _, n in blas if n), default=None)
+        blas_desc = ", ".join(f"{api} {n} threads" for api, n in blas) or "none loaded"
+    except Exception as e:  # threadpoolctl missing or failing: say so rather than guess
+        blas_threads, blas_desc = None, f"unknown ({type(e).__name__})"
+    used = max(1, round(cpu / wall))
     return {
-        "value": kv_bytes / wall / 1e9, "unit": "GB/s", "cores": max(1, round(cpu / wall)),
+        "value": kv_bytes / wall / 1e9, "unit": "GB/s", "cores": used,
         "kind": "oracle",
         "sample": f"{len(done)} sequence-steps ({passes} whole passes over the {w.num_seqs} sequences, then "
                   f"{len(done) - passes * w.num_seqs} more; reshape of the new token + fp64 decode each), "
-                  f"{wall:.1f} s wall, {cpu:.1f} s CPU, {len(os.sched_getaffinity(0))} host cores visible",
+                  f"{wall:.1f} s wall, {cpu:.1f} s CPU, {len(os.sched_getaffinity(0))} host cores visible; "
+                  f"the oracle's per-head products are small gemv calls, so it ran on {used} core(s) "
+                  f"although BLAS ({blas_desc}) could use more",
+        "blas_threads": blas_threads,
+        "host_cores_visible": len(os.sched_getaffinity(0)),
         "seq_steps_per_s": len(done) / wall,
     }
 
@@ -267,8 +280,7 @@ def main():
     from paged_kv_cache_380_amd import binding
     from paged_kv_cache_380_amd import workloads as wl
     binding.load()
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from pa_testlib import GpuCase
+    from paged_kv_cache_380_amd.resident import ResidentBatch as GpuCase
 
     if args.op == "prefill":
         return bench_prefill(args, dev)
@@ -431,8 +443,7 @@ def bench_prefill(args, dev):
     import torch
     from paged_kv_cache_380_amd import binding
     from paged_kv_cache_380_amd import workloads as wl
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from pa_testlib import GpuCase
+    from paged_kv_cache_380_amd.resident import ResidentBatch as GpuCase
     S, L, H, Hkv, D = 8, 2048, 32, 8, 128
     w = wl.build("prefill_llama3_8b_bf16_b8x2048", [L] * S, H, Hkv, D, "bf16", seed=6, free_fraction=0.05)
     log(f"[bench] building {w.name}")
@@ -523,8 +534,11 @@ def balanced_schedule(w, partition_blocks: int) -> bool:
 
 def append_fuses(w) -> bool:
     """Whether pa_decode_append writes the new rows inside the decode kernel (the library's rule, restated):
-    the vector-ALU kernel with one workgroup per KV head."""
+    the vector-ALU kernel with one workgroup per KV head, or the matrix-core kernel with one head tile per KV
+    head (4, 8 or 16 query heads per KV head)."""
     group = w.num_heads // w.num_kv_heads
+    if decode_kernel(w) == "decode_mfma":
+        return group in (4, 8, 16)
     tile = next(t for t in (8, 4, 2, 1) if group % t == 0)
     return decode_kernel(w) == "decode_main" and tile == group
 

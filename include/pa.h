@@ -284,15 +284,22 @@ size_t pa_decode_shared_prefix_workspace_bytes(int num_seqs, int num_heads, int 
  *                   negative slot writes nothing. Slot s must be the slot of
  *                   position context_lens[s] - 1 of sequence s (a decode step's
  *                   new token), in a block no other sequence of the batch reads
- *                   (its private last block, as after copy-on-write).
+ *                   (its private last block, as after copy-on-write). If it is
+ *                   not, the caches still end as pa_reshape_and_cache leaves
+ *                   them, but the output is undefined (a reader of that block
+ *                   may see the row before or after the write).
  *   others          as in pa_decode (k_cache, v_cache written as by
  *                   pa_reshape_and_cache; k_scale / v_scale also encode FP8)
  *
- * Where the vector-ALU kernel runs with one workgroup per (sequence, KV head)
- * -- MHA or two query heads per KV head with F16/BF16 queries, 1, 2, 4 or 8
- * with F32 queries -- that workgroup writes its KV head's new row before it
- * reads the block (one launch instead of two). Elsewhere the reshape kernel
- * runs first. Errors as in pa_reshape_and_cache and pa_decode.
+ * Where exactly one wave of the decode launch reads the block holding a
+ * sequence's new row for a KV head, the decode kernel writes the row itself,
+ * by that wave, which waits for its own stores to complete before it loads
+ * any block (one launch instead of two): the vector-ALU kernel with one
+ * workgroup per (sequence, KV head) -- MHA or two query heads per KV head
+ * with F16/BF16 queries, 1, 2, 4 or 8 with F32 queries -- and the matrix-core
+ * kernel with 4, 8 or 16 query heads per KV head, in either schedule.
+ * Elsewhere the reshape kernel runs first. Every argument is checked before
+ * anything is queued; errors as in pa_reshape_and_cache and pa_decode.
  */
 int pa_decode_append(void* out, const void* q, const void* key, const void* value, void* k_cache, void* v_cache,
                      const void* slot_mapping, int slot_is_int64, const int32_t* block_tables,

@@ -70,6 +70,18 @@ def quantize_for_cache(x_raw: np.ndarray, src_dtype: str, cache_dtype: str, scal
         return np.array(x_raw, copy=True)
     if cache_dtype != "fp8_e4m3" or src_dtype == "fp8_e4m3":
         raise ValueError(f"cannot store {src_dtype} activations in a {cache_dtype} cache")
+    if src_dtype in ("f16", "bf16"):
+        # The stored code is a function of the input's 16 bits alone: evaluate it once for each of the 65536
+        # bit patterns and look every element up (the same values as encoding element by element, without
+        # float64 temporaries the size of a whole cache).
+        patterns = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+        table = _quantize_e4m3(patterns if src_dtype == "bf16" else patterns.view(np.float16), src_dtype, scale)
+        return table[np.asarray(x_raw).view(np.uint16)]
+    return _quantize_e4m3(x_raw, src_dtype, scale)
+
+
+def _quantize_e4m3(x_raw: np.ndarray, src_dtype: str, scale: float) -> np.ndarray:
+    """E4M3 code of each element: float32 widening, |x| / scale in float32, sign put back, then encode."""
     x32 = widen(x_raw, src_dtype).astype(np.float32)  # exact: every source dtype fits in float32
     with np.errstate(invalid="ignore", over="ignore"):
         y = np.copysign(np.divide(np.abs(x32), np.float32(scale), dtype=np.float32), x32)

@@ -149,17 +149,11 @@ Layout workspace_layout(int num_seqs, int num_heads, int head_size, int max_bloc
   return L;
 }
 
-}  // namespace
-
-extern "C" {
-
-const char* pa_version(void) { return "0.1.0"; }
-
-int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
-                         const void* slot_mapping, int slot_is_int64, int64_t num_tokens,
-                         int num_kv_heads, int head_size, int64_t num_blocks, int block_size,
-                         pa_dtype kv_dtype, pa_dtype cache_dtype, float k_scale, float v_scale,
-                         void* stream) {
+// pa_reshape_and_cache's host checks (also run by pa_decode_append before it
+// launches anything). num_tokens == 0 passes without looking at the pointers.
+int reshape_check(const void* key, const void* value, const void* k_cache, const void* v_cache,
+                  const void* slot_mapping, int64_t num_tokens, int num_kv_heads, int head_size, int64_t num_blocks,
+                  int block_size, pa_dtype kv_dtype, pa_dtype cache_dtype, float k_scale, float v_scale) {
   if (num_tokens < 0 || num_kv_heads < 1 || num_blocks < 1)
     return fail(PA_ERR_SHAPE, "reshape_and_cache: bad sizes (num_tokens=%lld, num_kv_heads=%d, num_blocks=%lld)",
                 (long long)num_tokens, num_kv_heads, (long long)num_blocks);
@@ -183,11 +177,35 @@ int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void
                 (long long)num_tokens, num_kv_heads);
   if (!key || !value || !k_cache || !v_cache || !slot_mapping)
     return fail(PA_ERR_NULL, "reshape_and_cache: NULL pointer argument");
+  return ok();
+}
+
+int reshape_launch(const void* key, const void* value, void* k_cache, void* v_cache, const void* slot_mapping,
+                   int slot_is_int64, int64_t num_tokens, int num_kv_heads, int head_size, int64_t num_blocks,
+                   pa_dtype kv_dtype, pa_dtype cache_dtype, float k_scale, float v_scale, void* stream) {
   pa::ReshapeArgs a{key, value, k_cache, v_cache, slot_mapping, num_tokens, num_blocks, num_kv_heads, head_size,
                     slot_is_int64 ? 1 : 0, k_scale, v_scale};
   const hipError_t e = pa::launch_reshape(a, kv_dtype, cache_dtype, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "reshape_and_cache: launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_version(void) { return "0.1.0"; }
+
+int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                         const void* slot_mapping, int slot_is_int64, int64_t num_tokens,
+                         int num_kv_heads, int head_size, int64_t num_blocks, int block_size,
+                         pa_dtype kv_dtype, pa_dtype cache_dtype, float k_scale, float v_scale,
+                         void* stream) {
+  const int rc = reshape_check(key, value, k_cache, v_cache, slot_mapping, num_tokens, num_kv_heads, head_size,
+                               num_blocks, block_size, kv_dtype, cache_dtype, k_scale, v_scale);
+  if (rc != PA_OK || num_tokens == 0) return rc;
+  return reshape_launch(key, value, k_cache, v_cache, slot_mapping, slot_is_int64, num_tokens, num_kv_heads,
+                        head_size, num_blocks, kv_dtype, cache_dtype, k_scale, v_scale, stream);
 }
 
 int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_blocks, const int32_t* dst_blocks, int num_pairs,
@@ -300,19 +318,27 @@ size_t pa_decode_workspace_bytes(int num_seqs, int num_heads, int num_kv_heads, 
 
 namespace {
 
-// The new tokens of pa_decode_append (one per sequence), for the fused path.
+// The new tokens of pa_decode_append (one per sequence). fused: the decode
+// kernel writes them itself; otherwise the reshape kernel is queued first.
 struct Append {
   const void* key;
   const void* value;
+  void* k_cache;
+  void* v_cache;
   const void* slots;
   int slots_int64;
+  pa_dtype kv_dtype;
+  bool fused;
 };
 
 // pa_decode_split, pa_decode_shared_prefix and pa_decode_append: validation,
 // schedule choice, launch. groups (host, [num_groups][3]) name the
-// shared-prefix groups, or are NULL; app, when set, asks the decode kernel to
-// write the new tokens first (the caller has checked that the vector-ALU
-// kernel with one workgroup per KV head runs).
+// shared-prefix groups, or are NULL; app, when set, holds the step's new
+// tokens (the caller has checked them with reshape_check): a fused append
+// asks the decode kernel to write them (the caller has checked that a kernel
+// with one workgroup or wave per KV head and block runs), otherwise the
+// reshape kernel is queued before the decode kernels. Every check runs
+// before the first launch.
 int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
                 const int32_t* context_lens, float scale, int num_kv_heads, int block_size, int num_seqs,
                 int num_heads, int head_size, int max_blocks_per_seq, int64_t num_blocks, pa_dtype q_dtype,
@@ -444,7 +470,7 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
     a.grp_tile0[num_groups] = tiles;
     if (prefix_parts > 65535) return fail(PA_ERR_UNSUPPORTED, "decode: shared prefix too long");
   }
-  if (app) {
+  if (app && app->fused) {
     a.append = 1;
     a.new_key = app->key;
     a.new_value = app->value;
@@ -452,6 +478,11 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
     a.new_slots_int64 = app->slots_int64;
     a.enc_k_scale = k_scale;
     a.enc_v_scale = v_scale;
+  } else if (app) {
+    const int rc = reshape_launch(app->key, app->value, app->k_cache, app->v_cache, app->slots, app->slots_int64,
+                                  num_seqs, num_kv_heads, head_size, num_blocks, app->kv_dtype, cache_dtype, k_scale,
+                                  v_scale, stream);
+    if (rc != PA_OK) return rc;
   }
   const hipError_t e = pa::launch_decode(a, q_dtype, cache_dtype, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "decode: launch failed: %s", hipGetErrorString(e));
@@ -507,31 +538,23 @@ int pa_decode_append(void* out, const void* q, const void* key, const void* valu
                      int num_heads, int head_size, int max_blocks_per_seq, int64_t num_blocks, pa_dtype q_dtype,
                      pa_dtype cache_dtype, pa_dtype out_dtype, float k_scale, float v_scale, void* workspace,
                      size_t workspace_bytes, void* stream) {
-  // The decode kernel can write the new rows itself where it runs the vector-ALU
-  // kernel with one workgroup per (sequence, KV head, partition): only that
-  // workgroup then reads the block holding the new row for its KV head. That is
-  // MHA or two query heads per KV head with 16-bit queries, and groups of 1, 2,
-  // 4 or 8 with float32 queries. Elsewhere the rows are written by the reshape
-  // kernel first (two launches, same result).
+  // The decode kernel writes the new rows itself where exactly one wave of the
+  // launch reads the block holding a sequence's new row for a KV head: the
+  // vector-ALU kernel with one workgroup per (sequence, KV head, partition)
+  // (MHA or two query heads per KV head with 16-bit queries; groups of 1, 2,
+  // 4 or 8 with float32 queries), and the matrix-core kernel with one head
+  // tile per KV head (groups of 4, 8 or 16), in either schedule. Elsewhere the
+  // reshape kernel runs first (two launches, same result).
   const int group = num_kv_heads >= 1 && num_heads % num_kv_heads == 0 ? num_heads / num_kv_heads : 0;
   const bool sixteen = q_dtype == PA_DTYPE_F16 || q_dtype == PA_DTYPE_BF16;
-  const bool fused = group > 0 && !use_mfma(q_dtype, group) && pa::group_tile_for(group) == group &&
-                     !(group >= 4 && sixteen);
-  if (num_seqs > 0 && (!key || !value || !slot_mapping))
-    return fail(PA_ERR_NULL, "decode_append: NULL key, value or slot_mapping");
-  if (!fused) {
-    const int rc = pa_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, slot_is_int64, num_seqs,
-                                        num_kv_heads, head_size, num_blocks, block_size, q_dtype, cache_dtype,
-                                        k_scale, v_scale, stream);
-    if (rc != PA_OK) return rc;
-    return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, scale, num_kv_heads, block_size,
-                       num_seqs, num_heads, head_size, max_blocks_per_seq, num_blocks, q_dtype, cache_dtype,
-                       out_dtype, k_scale, v_scale, 0, nullptr, 0, workspace, workspace_bytes, stream);
-  }
-  if (cache_dtype == PA_DTYPE_FP8_E4M3 &&
-      !(std::isfinite(k_scale) && std::isfinite(v_scale) && k_scale > 0.f && v_scale > 0.f))
-    return fail(PA_ERR_SHAPE, "decode_append: FP8 scales must be finite and positive");
-  const Append app{key, value, slot_mapping, slot_is_int64 ? 1 : 0};
+  const bool mfma = group > 0 && use_mfma(q_dtype, group);
+  const bool fused = group > 0 && (mfma ? pa::mfma_group_tile(group) == group
+                                        : pa::group_tile_for(group) == group && !(group >= 4 && sixteen));
+  if (num_seqs < 0) return fail(PA_ERR_SHAPE, "decode_append: num_seqs must be >= 0 (got %d)", num_seqs);
+  const int rc = reshape_check(key, value, k_cache, v_cache, slot_mapping, num_seqs, num_kv_heads, head_size,
+                               num_blocks, block_size, q_dtype, cache_dtype, k_scale, v_scale);
+  if (rc != PA_OK) return rc;
+  const Append app{key, value, k_cache, v_cache, slot_mapping, slot_is_int64 ? 1 : 0, q_dtype, fused};
   return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, scale, num_kv_heads, block_size, num_seqs,
                      num_heads, head_size, max_blocks_per_seq, num_blocks, q_dtype, cache_dtype, out_dtype, k_scale,
                      v_scale, 0, nullptr, 0, workspace, workspace_bytes, stream, &app);

@@ -163,36 +163,6 @@ __device__ __forceinline__ float swap_sum16(float a, float b) {
 constexpr int kDppRowRor8 = 0x128;  // lane j <- lane (j - 8) mod 16, i.e. j ^ 8
 constexpr int kDppRowRor4 = 0x124;  // lane j <- lane (j - 4) mod 16
 
-// Fused append: write sequence seq's new K and V rows of KV head kvh into the
-// cache slot a.new_slots[seq] (bit copy, or E4M3 after dividing by the scale,
-// exactly as reshape_kernel does), one 16-byte source chunk per thread of
-// the N taking part (thread index tid).
-template <int QK, int CK, int D, int N>
-__device__ __forceinline__ void append_row(const DecodeArgs& a, int seq, int kvh, int tid) {
-  const int64_t slot = a.new_slots_int64 ? static_cast<const int64_t*>(a.new_slots)[seq]
-                                         : (int64_t) static_cast<const int32_t*>(a.new_slots)[seq];
-  if (slot < 0 || slot >= a.num_blocks * 16) return;
-  constexpr int kSrc = KindBytes<QK>::value;
-  constexpr int E = 16 / kSrc;  // source elements per chunk
-  constexpr int NC = D / E;     // chunks per row
-  const int64_t src = ((int64_t)seq * a.num_kv_heads + kvh) * D;
-  const int64_t dst = (((slot >> 4) * a.num_kv_heads + kvh) * 16 + (slot & 15)) * D;
-  for (int i = tid; i < 2 * NC; i += N) {
-    const bool is_v = i >= NC;
-    const int c = is_v ? i - NC : i;
-    const uint4 x = *reinterpret_cast<const uint4*>(static_cast<const char*>(is_v ? a.new_value : a.new_key) +
-                                                     (src + (int64_t)c * E) * kSrc);
-    char* cache = static_cast<char*>(const_cast<void*>(is_v ? a.v_cache : a.k_cache));
-    if constexpr (CK == QK) {
-      *reinterpret_cast<uint4*>(cache + (dst + (int64_t)c * E) * kSrc) = x;
-    } else if constexpr (CK == kFP8 && QK == kF32) {
-      *reinterpret_cast<uint32_t*>(cache + dst + (int64_t)c * E) = e4m3_chunk32(x, is_v ? a.enc_v_scale : a.enc_k_scale);
-    } else if constexpr (CK == kFP8) {
-      *reinterpret_cast<uint2*>(cache + dst + (int64_t)c * E) = e4m3_chunk16<QK>(x, is_v ? a.enc_v_scale : a.enc_k_scale);
-    }
-  }
-}
-
 template <int QK, int CK, int D, int GT>
 __global__ __launch_bounds__(kThreads) void decode_main(const DecodeArgs a) {
   using Geo = TileGeo<CK, D>;
@@ -219,10 +189,10 @@ __global__ __launch_bounds__(kThreads) void decode_main(const DecodeArgs a) {
   // Fused append: the new row (position ctx - 1) lies in the sequence's last
   // block, which for this KV head only one wave of the launch reads (one
   // workgroup per KV head; the last partition's wave (nblk - 1) % kWaves, at
-  // the end of its stream). That wave writes the row first; its own later
-  // load of the block sees the stores (wavefront-scope release / acquire),
-  // and the other waves start streaming at once. An empty context's row goes
-  // out with partition 0.
+  // the end of its stream). That wave writes the row and waits until its
+  // stores have completed before it issues any load, so its later load of
+  // the block returns the new row; the other waves start streaming at once.
+  // An empty context's row goes out with partition 0.
   const bool writer = a.append && part == (ctx > 0 ? (((ctx + 15) >> 4) - 1) / a.partition_blocks : 0);
   if (ctx <= 0) {  // nothing to attend
     if (writer) append_row<QK, CK, D, kThreads>(a, seq, kvh, tid);
@@ -260,8 +230,7 @@ __global__ __launch_bounds__(kThreads) void decode_main(const DecodeArgs a) {
   // (After the barrier, so that only the writing wave waits for its stores.)
   if (writer && wave == (nblk - 1) % kWaves) {
     append_row<QK, CK, D, 64>(a, seq, kvh, lane);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    wait_own_stores();
   }
 
   float m[GT], l[GT], acc[GT][E];

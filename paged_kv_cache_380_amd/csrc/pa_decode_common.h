@@ -146,6 +146,46 @@ __device__ __forceinline__ void stream_blocks(int first, int step, int n, Load&&
   }
 }
 
+// Waits until every vector memory operation this wave has issued, stores
+// included, has completed (s_waitcnt vmcnt(0); gfx9 counts stores in vmcnt).
+// After it, a load by this wave of an address the wave just stored to returns
+// the stored data: the store is complete at the L2 that serves the load, and
+// the write-through L1 holds no older copy of a line this wave never read.
+__device__ __forceinline__ void wait_own_stores() {
+  // simm16 on gfx9: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] at [15:14].
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt not waited for
+}
+
+// Fused append: write sequence seq's new K and V rows of KV head kvh into the
+// cache slot a.new_slots[seq] (bit copy, or E4M3 after dividing by the scale,
+// exactly as reshape_kernel does), one 16-byte source chunk per thread of
+// the N taking part (thread index tid).
+template <int QK, int CK, int D, int N>
+__device__ __forceinline__ void append_row(const DecodeArgs& a, int seq, int kvh, int tid) {
+  const int64_t slot = a.new_slots_int64 ? static_cast<const int64_t*>(a.new_slots)[seq]
+                                         : (int64_t) static_cast<const int32_t*>(a.new_slots)[seq];
+  if (slot < 0 || slot >= a.num_blocks * 16) return;
+  constexpr int kSrc = KindBytes<QK>::value;
+  constexpr int E = 16 / kSrc;  // source elements per chunk
+  constexpr int NC = D / E;     // chunks per row
+  const int64_t src = ((int64_t)seq * a.num_kv_heads + kvh) * D;
+  const int64_t dst = (((slot >> 4) * a.num_kv_heads + kvh) * 16 + (slot & 15)) * D;
+  for (int i = tid; i < 2 * NC; i += N) {
+    const bool is_v = i >= NC;
+    const int c = is_v ? i - NC : i;
+    const uint4 x = *reinterpret_cast<const uint4*>(static_cast<const char*>(is_v ? a.new_value : a.new_key) +
+                                                     (src + (int64_t)c * E) * kSrc);
+    char* cache = static_cast<char*>(const_cast<void*>(is_v ? a.v_cache : a.k_cache));
+    if constexpr (CK == QK) {
+      *reinterpret_cast<uint4*>(cache + (dst + (int64_t)c * E) * kSrc) = x;
+    } else if constexpr (CK == kFP8 && QK == kF32) {
+      *reinterpret_cast<uint32_t*>(cache + dst + (int64_t)c * E) = e4m3_chunk32(x, is_v ? a.enc_v_scale : a.enc_k_scale);
+    } else if constexpr (CK == kFP8) {
+      *reinterpret_cast<uint2*>(cache + dst + (int64_t)c * E) = e4m3_chunk16<QK>(x, is_v ? a.enc_v_scale : a.enc_k_scale);
+    }
+  }
+}
+
 // Zeros for a sequence with nothing to attend, written once (by partition 0).
 template <int GT, int D>
 __device__ __forceinline__ void write_zeros(const DecodeArgs& a, int seq, int h0, int part, int tid) {

@@ -504,7 +504,13 @@ __global__ __launch_bounds__(kThreads) void decode_mfma(const DecodeArgs a) {
   } else if constexpr (!kBalanced) {
     // One partition of one sequence; the four waves take its blocks in turn.
     ctx = context_len(a, seq);
+    // Fused append (one workgroup per KV head): the new row lies in the
+    // sequence's last block, read only by wave (nblk - 1) % kWaves of the
+    // last partition; that wave writes it and waits for its stores before it
+    // loads anything. An empty context's row goes out with partition 0.
+    const bool writer = a.append && part == (ctx > 0 ? (((ctx + 15) >> 4) - 1) / a.partition_blocks : 0);
     if (ctx <= 0) {
+      if (writer) append_row<QK, CK, D, kThreads>(a, seq, kvh, tid);
       write_zeros<GT, D>(a, seq, h0, part, tid);
       return;
     }
@@ -518,6 +524,10 @@ __global__ __launch_bounds__(kThreads) void decode_mfma(const DecodeArgs a) {
     for (int j = tid; j < nblk; j += kThreads) s_blocks[j] = bt[j];
     load_q(seq);
     __syncthreads();
+    if (writer && wave == (nblk - 1) % kWaves) {
+      append_row<QK, CK, D, 64>(a, seq, kvh, lane);
+      wait_own_stores();
+    }
 
     reset();
     run_blocks(wave, kWaves, nblk, seq_blocks);
@@ -606,6 +616,14 @@ __global__ __launch_bounds__(kThreads) void decode_mfma(const DecodeArgs a) {
     };
     if (blockIdx.x == 0 && blockIdx.y == 0)
       for (int k = tid; k <= S; k += kThreads) a.ws_pref[k] = s_pref[k];
+    // Fused append (one wave per KV head and range): the wave whose range
+    // holds a sequence's last block writes that sequence's new row below,
+    // before it loads any block of it. Sequences with no block in any range
+    // (empty contexts) are read by no wave; their rows are written here, by
+    // the first workgroup of each KV head, one thread per sequence.
+    if (a.append && part == 0)
+      for (int s = tid; s < S; s += kThreads)
+        if (s_pref[s] == s_pref[s + 1]) append_row<QK, CK, D, 1>(a, s, kvh, 0);
 
     // Each wave stages the block ids of its range in LDS, a window of
     // kWindow positions at a time (no workgroup barrier: the window is the
@@ -634,6 +652,10 @@ __global__ __launch_bounds__(kThreads) void decode_mfma(const DecodeArgs a) {
       const int piece_end = min(r_end, pe);
       const int shb = s_shr[seq];  // position ps is block shb of the sequence
       ctx = context_len(a, seq);
+      if (a.append && piece_end == pe) {  // this range holds the sequence's last block
+        append_row<QK, CK, D, 64>(a, seq, kvh, lane);
+        wait_own_stores();
+      }
       load_q(seq);
       reset();
       // The piece [pos, piece_end), window by window, accumulating throughout.

@@ -71,10 +71,12 @@ struct DecodeArgs {
   int grp_count[kMaxPrefixGroups];
   int grp_blocks[kMaxPrefixGroups];     // shared full blocks of group g
   int grp_tile0[kMaxPrefixGroups + 1];  // first prefix-kernel tile of group g (tiles of 16 / group sequences)
-  // Fused append (pa_decode_append, vector-ALU kernel with one workgroup per
-  // (sequence, KV head, partition)): the workgroup of the partition holding a
-  // sequence's last block first writes that sequence's new K/V row of its KV
-  // head into the cache (as pa_reshape_and_cache would), then attends.
+  // Fused append (pa_decode_append, where one wave of the launch reads each
+  // (sequence, KV head)'s last block: the vector-ALU kernel with one
+  // workgroup per (sequence, KV head, partition), or the matrix-core kernel
+  // with one head tile per KV head): that wave first writes the sequence's
+  // new K/V row of its KV head into the cache (as pa_reshape_and_cache
+  // would) and waits for the stores, then attends.
   int append;
   int new_slots_int64;    // slot type: int64 (1) or int32 (0)
   const void* new_key;    // [S, Hkv, D], the query dtype

@@ -239,3 +239,35 @@ def test_shared_prefix_workspace(lib):
     # cache takes the range count the plain size is computed for)
     assert shared(lib, [(0, 8, 5)], ws=FAKE, wsb=base, cd=3) == 5
     assert "workspace" in lib.pa_last_error().decode()
+
+
+def append(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, key=FAKE, value=FAKE, kc=FAKE, vc=FAKE, slots=FAKE, i64=1, bt=FAKE, cl=FAKE,
+             scale=0.125, Hkv=2, B=16, S=4, H=8, D=128, M=8, N=64, qd=1, cd=1, od=1, ks=1.0, vs=1.0, ws=None, wsb=0,
+             stream=None)
+    a.update(kw)
+    return lib.pa_decode_append(a["out"], a["q"], a["key"], a["value"], a["kc"], a["vc"], a["slots"], a["i64"],
+                                a["bt"], a["cl"], a["scale"], a["Hkv"], a["B"], a["S"], a["H"], a["D"], a["M"], a["N"],
+                                a["qd"], a["cd"], a["od"], a["ks"], a["vs"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(key=None), 1), (dict(value=None), 1), (dict(slots=None), 1), (dict(q=None), 1), (dict(out=None), 1),
+    (dict(cd=3, ks=0.0), 3), (dict(cd=3, vs=float("nan")), 3), (dict(cd=3, ks=-2.0, qd=2), 3),
+    (dict(od=2), 2), (dict(qd=0, cd=3), 2), (dict(qd=2, cd=1), 2), (dict(B=8), 4), (dict(D=80), 4),
+    (dict(S=-1), 3), (dict(H=6, Hkv=4), 3), (dict(scale=float("inf")), 3),
+    # grouped queries on the matrix cores, fused path: a context spanning several partitions needs a workspace
+    (dict(H=8, Hkv=2, qd=2, cd=2, od=2, M=64), 5), (dict(H=8, Hkv=2, qd=2, cd=2, od=2, M=64, ws=FAKE, wsb=64), 5),
+    # the two-launch path (6 query heads per KV head) checks everything before it queues the reshape kernel
+    (dict(H=12, Hkv=2, qd=2, cd=2, od=2, M=64), 5), (dict(H=12, Hkv=2, qd=2, cd=2, od=1), 2),
+    (dict(H=12, Hkv=2, qd=2, cd=3, ks=0.0, od=2), 3), (dict(H=12, Hkv=2, qd=2, cd=2, od=2, scale=float("nan")), 3),
+])
+def test_decode_append_rejects(lib, kw, code):
+    # Every check runs before anything is queued: these calls must fail validation on a machine without a GPU
+    # (a launch attempt would instead report PA_ERR_LAUNCH).
+    assert append(lib, **kw) == code
+    assert lib.pa_last_error().decode()
+
+
+def test_decode_append_zero_seqs_is_a_no_op(lib):
+    assert append(lib, S=0, out=None, q=None, key=None, value=None, slots=None) == 0

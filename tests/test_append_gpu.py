@@ -1,13 +1,16 @@
 """pa_decode_append (a whole decode step: append the newest token, then attend) against the oracle and
 against pa_reshape_and_cache followed by pa_decode.
 
-Where the vector-ALU kernel runs with one workgroup per (sequence, KV head), the decode kernel writes the new
-rows itself (one launch); elsewhere the reshape kernel runs first. Either way the caches must equal the
-oracle's byte for byte, the output must match the oracle, and it must equal the two-call result bit for bit
-(the attention arithmetic is the same). Cases: MHA and two query heads per KV head in 16 bits (fused), float32
-with 1 to 8 query heads per KV head (fused), an FP8 cache written by the fused path, contexts split over
-partitions (the last partition's workgroup writes), empty sequences and negative slots, int32 slots, grouped
-queries on the matrix cores (two launches), and the Llama-2-7B-shaped batch at full size.
+Where exactly one wave of the decode launch reads the block holding a sequence's new row for a KV head, the
+decode kernel writes the rows itself (one launch): the vector-ALU kernel with one workgroup per (sequence, KV
+head), and the matrix-core kernel with 4, 8 or 16 query heads per KV head, in its balanced schedule (the wave
+whose range holds the last block writes) and in its partitioned one (the wave of the last partition that takes
+the last block writes). Elsewhere the reshape kernel runs first. Either way the caches must equal the oracle's
+byte for byte, the output must match the oracle, and it must equal the two-call result bit for bit (the
+attention arithmetic is the same). Cases: MHA and two query heads per KV head in 16 bits, float32 with 1 to 8
+query heads per KV head, FP8 caches, contexts split over partitions, empty sequences and negative slots, int32
+slots, grouped queries on the matrix cores in both schedules, two-launch shapes (6 and 32 query heads per KV
+head), and the Llama-2-7B, Llama-3-8B and prefix-sharing FP8 batches at full size.
 """
 
 import numpy as np
@@ -30,14 +33,20 @@ def need_gpu():
     torch.cuda.synchronize()
 
 
-def run(w: wl.Workload, slot_dtype=torch.int64, check_oracle=True):
+def run(w: wl.Workload, slot_dtype=torch.int64, check_oracle=True, workspace_bytes=None):
+    """One step through pa_decode_append and through reshape + decode (same workspace size, so the same
+    schedule), compared with each other and with the oracle. workspace_bytes: None for the library's default
+    size; a smaller size selects the partitioned schedule."""
     from paged_kv_cache_380_amd import binding
+    ws = None if workspace_bytes is None else torch.empty(workspace_bytes, dtype=torch.uint8, device="cuda")
     fused = GpuCase(w, slot_dtype=slot_dtype)
     out = torch.full(fused.q.shape, float("nan"), dtype=torch.float32, device="cuda")
     binding.decode_append(out, fused.q, fused.new_key, fused.new_value, fused.kc, fused.vc, fused.new_slots,
-                          fused.tables, fused.lens, w.scale, w.num_kv_heads, w.block_size, w.k_scale, w.v_scale)
+                          fused.tables, fused.lens, w.scale, w.num_kv_heads, w.block_size, w.k_scale, w.v_scale,
+                          workspace=ws)
     two = GpuCase(w, slot_dtype=slot_dtype)
-    ref_gpu = two.step(out_dtype=torch.float32)
+    two.append()
+    ref_gpu = two.decode(out_dtype=torch.float32, workspace=ws)
     torch.cuda.synchronize()
     kc, vc = oracle_fill(w)
     assert np.array_equal(raw(fused.kc).view(np.uint8), kc.view(np.uint8)), f"{w.name}: K cache differs"
@@ -67,14 +76,45 @@ def test_split_contexts_empty_sequences_and_int32_slots():
     run(w, slot_dtype=torch.int32)
 
 
-@pytest.mark.parametrize("H,Hkv,cache", [(32, 8, "bf16"), (32, 8, "fp8_e4m3"), (12, 2, "bf16")])
-def test_two_launch_shapes(H, Hkv, cache):
-    # grouped queries on the matrix cores, or groups of 6 on the vector ALU with several workgroups per KV head
+@pytest.mark.parametrize("H,Hkv,cache", [(32, 8, "bf16"), (32, 8, "fp8_e4m3"), (64, 4, "bf16"), (16, 1, "f16"),
+                                         (12, 2, "bf16"), (64, 2, "bf16"), (128, 1, "fp8_e4m3")])
+def test_grouped_shapes(H, Hkv, cache):
+    # 4, 8 and 16 query heads per KV head run fused on the matrix cores (balanced schedule); 6 (vector ALU,
+    # several workgroups per KV head), 32 and 128 (several matrix-core waves per KV head) take two launches
     rng = np.random.default_rng(H + Hkv)
-    w = wl.build(f"append_two_{H}_{Hkv}_{cache}", [int(rng.integers(0, 900)) for _ in range(11)], H, Hkv, 128,
-                 "bf16", cache_dtype=cache, seed=43, free_fraction=0.1, kv_scale=0.05)
+    dtype = "f16" if cache == "f16" else "bf16"
+    w = wl.build(f"append_grp_{H}_{Hkv}_{cache}", [int(rng.integers(0, 900)) for _ in range(11)] + [0, 1, 16, 17],
+                 H, Hkv, 128, dtype, cache_dtype=cache, seed=43, free_fraction=0.1, kv_scale=0.05)
     run(w)
 
 
-def test_llama7b_mha_full_size():
-    run(wl.llama7b_mha_fp16())
+@pytest.mark.parametrize("H,Hkv,cache", [(32, 8, "bf16"), (16, 4, "fp8_e4m3"), (64, 4, "f16")])
+def test_grouped_partitioned_schedule(H, Hkv, cache):
+    # a workspace too small for the balanced schedule but enough for the partitioned one: the matrix-core
+    # kernel runs one workgroup per (sequence, KV head, partition), and the last partition's writer wave
+    # appends; long contexts are split, so the merge kernel runs too
+    from paged_kv_cache_380_amd import binding
+    dtype = "f16" if cache == "f16" else "bf16"
+    lens = [5000, 17, 0, 3000, 301, 1, 4096]
+    w = wl.build(f"append_part_{H}_{Hkv}_{cache}", lens, H, Hkv, 128, dtype, cache_dtype=cache, seed=44,
+                 free_fraction=0.1, kv_scale=0.05)
+    pb = binding.decode_partition_blocks(w.num_seqs, H, Hkv, 128, w.max_blocks_per_seq)
+    part = binding.decode_workspace_bytes(w.num_seqs, H, Hkv, 128, w.max_blocks_per_seq, 16, pb)
+    full = binding.decode_workspace_bytes(w.num_seqs, H, Hkv, 128, w.max_blocks_per_seq)
+    assert 0 < part < full, (part, full)
+    run(w, workspace_bytes=part)
+
+
+def test_grouped_partitioned_no_workspace():
+    # 128 sequences x 8 KV heads fill the chip without splitting a context: no workspace at all, so the
+    # partitioned schedule runs with one partition per sequence
+    rng = np.random.default_rng(45)
+    w = wl.build("append_nows", [int(rng.integers(0, 400)) for _ in range(128)], 32, 8, 128, "bf16", seed=45,
+                 free_fraction=0.1)
+    run(w, workspace_bytes=0)
+
+
+@pytest.mark.parametrize("name", ["llama7b_mha_fp16", "llama3_8b_gqa_bf16", "prefix_fp8"])
+def test_full_size(name):
+    print(f"[append] {name}", flush=True)
+    run(wl.named(name))

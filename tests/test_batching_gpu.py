@@ -11,7 +11,9 @@ the CPU. Both caches must stay byte-identical and every decode must match.
 Each step also lists the batch with the forks of one prompt side by side, asks
 the block manager for the shared-prefix groups of that order
 (pa_bm_shared_prefix) and decodes it through pa_decode_shared_prefix, which
-must give pa_decode's result.
+must give pa_decode's result. Every step also runs through pa_decode_append on
+copies of the caches (one call: append, then attend), which must leave the
+same caches and give the same output bit for bit.
 """
 
 import itertools
@@ -40,7 +42,8 @@ def need_gpu():
 
 @pytest.mark.parametrize("H,Hkv,D,dtype,cache,path", [
     (8, 2, 128, "bf16", "bf16", "mfma"), (8, 2, 128, "bf16", "bf16", "valu"), (8, 8, 128, "f16", "f16", "auto"),
-    (16, 2, 128, "bf16", "fp8_e4m3", "mfma"), (4, 4, 64, "f32", "f32", "auto"),
+    (16, 2, 128, "bf16", "fp8_e4m3", "mfma"), (4, 4, 64, "f32", "f32", "auto"), (16, 8, 128, "f16", "f16", "auto"),
+    (32, 2, 64, "bf16", "bf16", "mfma"),
 ])
 def test_continuous_batching_steps(H, Hkv, D, dtype, cache, path, monkeypatch):
     from paged_kv_cache_380_amd import binding
@@ -61,10 +64,12 @@ def test_continuous_batching_steps(H, Hkv, D, dtype, cache, path, monkeypatch):
     root = {}  # the prompt a sequence descends from
     grouped = 0
 
-    def write(seqs_slots):
+    def draw(n):
+        return (torch.randn((n, Hkv, D), generator=gen).to(tdt), torch.randn((n, Hkv, D), generator=gen).to(tdt))
+
+    def write(seqs_slots, kv=None):
         slots = np.asarray(seqs_slots, dtype=np.int64)
-        k = torch.randn((len(slots), Hkv, D), generator=gen).to(tdt)
-        v = torch.randn((len(slots), Hkv, D), generator=gen).to(tdt)
+        k, v = kv if kv is not None else draw(len(slots))
         binding.reshape_and_cache(k.cuda(), v.cuda(), kc_d, vc_d, torch.from_numpy(slots).cuda(), kscale, vscale)
         oracle.reshape_and_cache(raw(k), raw(v), kc_o, vc_o, slots, B, dtype, cache, kscale, vscale)
 
@@ -95,12 +100,24 @@ def test_continuous_batching_steps(H, Hkv, D, dtype, cache, path, monkeypatch):
             binding.copy_blocks(kc_d, vc_d, torch.from_numpy(src).cuda(), torch.from_numpy(dst).cuda())
             oracle.copy_blocks(kc_o, vc_o, src, dst)
             copies += len(src)
-        write(slots)
+        # The same step through pa_decode_append on copies of the caches, as the block manager left them
+        # (copy-on-write done, the new token's slot in a private last block).
+        new_kv = draw(len(live))
+        kc_f, vc_f = kc_d.clone(), vc_d.clone()
+        write(slots, new_kv)
         tables, lens = bm.block_tables(live)
         q = torch.randn((len(live), H, D), generator=gen).to(tdt)
         out = torch.empty((len(live), H, D), dtype=torch.float32, device="cuda")
         binding.decode(out, q.cuda(), kc_d, vc_d, torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda(),
                        scale, Hkv, B, kscale, vscale)
+        out_f = torch.empty_like(out)
+        binding.decode_append(out_f, q.cuda(), new_kv[0].cuda(), new_kv[1].cuda(), kc_f, vc_f,
+                              torch.from_numpy(slots).cuda(), torch.from_numpy(tables).cuda(),
+                              torch.from_numpy(lens).cuda(), scale, Hkv, B, kscale, vscale)
+        assert torch.equal(out_f, out), f"step {step}: pa_decode_append differs from reshape + decode"
+        assert torch.equal(kc_f.view(torch.uint8), kc_d.view(torch.uint8)) and \
+            torch.equal(vc_f.view(torch.uint8), vc_d.view(torch.uint8)), f"step {step}: pa_decode_append caches differ"
+        del kc_f, vc_f
         ref = oracle.decode_attention(raw(q), kc_o, vc_o, tables, lens, scale, Hkv, B, dtype, cache, kscale, vscale)
         got = out.cpu().numpy()
         assert np.isfinite(got).all(), f"step {step}: non-finite output"

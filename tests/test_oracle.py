@@ -421,6 +421,27 @@ def pin_fp8_cache_quantisation(O):
     x = torch.from_numpy(raw(w.fill_key).view(np.int16)).view(torch.bfloat16).to(torch.float32)
     y = (x / torch.tensor(w.k_scale, dtype=torch.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     assert np.array_equal(codes, y)
+    # Every 16-bit input pattern, stored from bf16 and from f16 activations: the code equals torch's cast of
+    # the float32 quotient wherever that cast saturates properly (|x / s| <= 448; above, torch gives NaN for
+    # some values, and saturation is pinned apart), and equals what the same values give as float32 input.
+    scale = 0.05
+    pat = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    for src in ("bf16", "f16"):
+        x_raw = (pat if src == "bf16" else pat.view(np.float16)).reshape(512, 1, 128)
+        kc = np.zeros((32, 1, 16, 128), np.uint8)
+        vc = kc.copy()
+        O.reshape_and_cache(x_raw, x_raw, kc, vc, np.arange(512), 16, src, "fp8_e4m3", scale, scale)
+        got = kc.reshape(-1)
+        x32 = torch.from_numpy(pat.view(np.int16)).view(torch.bfloat16).float() if src == "bf16" else \
+            torch.from_numpy(pat.view(np.float16).copy()).float()
+        q = x32 / torch.tensor(scale, dtype=torch.float32)
+        ok = torch.isfinite(q) & (q.abs() <= 448)
+        want = q.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(got[ok.numpy()], want[ok.numpy()]), src
+        kf = np.zeros_like(kc)
+        O.reshape_and_cache(x32.numpy().reshape(512, 1, 128), x32.numpy().reshape(512, 1, 128), kf, vc.copy(),
+                            np.arange(512), 16, "f32", "fp8_e4m3", scale, scale)
+        assert np.array_equal(kf, kc), src
 
 
 PINS = [
@@ -538,6 +559,7 @@ MUTANTS = {
     "e4m3 bias 8": ("2.0 ** (exp_field - 7)", "2.0 ** (exp_field - 8)"),
     "e4m3 round half up": ("mag = np.rint(a / quantum) * quantum", "mag = np.floor(a / quantum + 0.5) * quantum"),
     "e4m3 no saturation": ("mag = np.where(a > E4M3_MAX, E4M3_MAX, mag)", "mag = np.where(a > E4M3_MAX, 0.0, mag)"),
+    "fp8 table: f16 bits read as bf16": ('patterns.view(np.float16), src_dtype, scale)', 'patterns, "bf16", scale)'),
     "copy: V not copied": ("v_cache[dst] = v_cache[src]", "v_cache[dst] = v_cache[dst]"),
     "copy: direction reversed": ("k_cache[dst] = k_cache[src]", "k_cache[src] = k_cache[dst]"),
     "prefill: causal limit one short": ("logits = scale64 * (keys[:p + 1, kv, :] @ qs[h])",

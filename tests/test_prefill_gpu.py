@@ -116,3 +116,43 @@ def test_empty_and_cut_chunks():
     assert np.abs(got[:4] - ref[:4]).max() <= 2e-3
     assert np.abs(got[4:10] - ref[4:10]).max() <= 2e-3     # first 6 rows of the 9-token chunk
     assert np.isnan(got[10:]).all()                         # rows past max_query_len are not written
+
+
+def test_prefill_benchmark_size():
+    # The benchmarked launch: 8 prompts of 2048 tokens as one chunk each, 32 query heads over 8 KV heads, bf16.
+    # The oracle takes the last 64 rows of every prompt (a 64-token chunk at the end of the context attends
+    # exactly as those rows of the full prompt do) and single rows 0, 1, 15, 16, 17 and 1000 of every prompt
+    # (a one-token chunk over a context of row + 1 tokens).
+    S, L, H, Hkv, D = 8, 2048, 32, 8, 128
+    w = wl.build("prefill_llama3_8b_bf16_b8x2048", [L] * S, H, Hkv, D, "bf16", seed=6, free_fraction=0.05)
+    case = GpuCase(w)
+    case.append()
+    q = torch.randn((S * L, H, D), generator=torch.Generator().manual_seed(7)).to(torch.bfloat16)
+    starts = np.arange(0, S * L + 1, L, dtype=np.int32)
+    got = run(case, q, starts, L).cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all(), "non-finite output"
+    native = run(case, q, starts, L, out_dtype=torch.bfloat16)
+    assert torch.equal(native, torch.from_numpy(got.astype(np.float32)).cuda().to(torch.bfloat16)), \
+        "native output is not the rounded float32 output"
+
+    tail, singles = 64, [0, 1, 15, 16, 17, 1000]
+    rows, tables, lens, qlens = [], [], [], []
+    for s in range(S):
+        rows += [s * L + r for r in range(L - tail, L)]
+        tables.append(w.block_tables[s].numpy())
+        lens.append(L)
+        qlens.append(tail)
+    for s in range(S):
+        for r in singles:
+            rows.append(s * L + r)
+            tables.append(w.block_tables[s].numpy())
+            lens.append(r + 1)
+            qlens.append(1)
+    kc, vc = oracle_fill(w)
+    ostarts = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int64)
+    ref = oracle.prefill_attention(raw(q)[rows], kc, vc, np.stack(tables), np.asarray(lens), ostarts, w.scale,
+                                   Hkv, 16, "bf16", "bf16")
+    err = float(np.abs(got[rows] - ref).max())
+    print(f"[prefill] 8 x 2048 benchmark launch, {len(rows)} rows against the oracle: max|err|={err:.3e}",
+          flush=True)
+    assert err <= tolerance(w), err
