@@ -308,6 +308,33 @@ int pa_decode_append(void* out, const void* q, const void* key, const void* valu
                      pa_dtype cache_dtype, pa_dtype out_dtype, float k_scale, float v_scale, void* workspace,
                      size_t workspace_bytes, void* stream);
 
+/*
+ * pa_decode_scratch -- pa_decode for callers that cannot allocate device
+ * memory around a call (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): no workspace argument; the library's own
+ * fixed scratch array serves as the workspace. Same arguments, result and
+ * schedule choice as pa_decode with a workspace of pa_decode_scratch_bytes()
+ * bytes; nothing is allocated or freed.
+ *
+ * The array lives in the library's device code, one copy per GPU, each held
+ * until the process ends; its address on a device is looked up on the first
+ * call with that device current, so the call must be made with the device
+ * that `stream` belongs to current. Shapes whose workspace need exceeds the
+ * array return PA_ERR_WORKSPACE with the sizes in the message (nothing
+ * queued). Every call on one GPU uses that GPU's one array: calls that can
+ * overlap on one GPU (other streams, other threads) race and must be
+ * serialised by the caller; calls queued on one stream are ordered. The array
+ * keeps the last call's contents; no call relies on them.
+ */
+int pa_decode_scratch(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens, float scale, int num_kv_heads,
+                      int block_size, int num_seqs, int num_heads, int head_size, int max_blocks_per_seq,
+                      int64_t num_blocks, pa_dtype q_dtype, pa_dtype cache_dtype, pa_dtype out_dtype, float k_scale,
+                      float v_scale, void* stream);
+
+/* Size of pa_decode_scratch's fixed scratch array, in bytes (32 MiB). */
+size_t pa_decode_scratch_bytes(void);
+
 /* Partition length (in blocks) pa_decode would choose for these shapes. */
 int pa_decode_partition_blocks(int num_seqs, int num_heads, int num_kv_heads, int head_size,
                                int max_blocks_per_seq, int block_size);

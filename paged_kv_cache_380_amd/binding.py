@@ -22,7 +22,7 @@ STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_DTYPE", 3: "PA_ERR_SHAPE", 4:
 
 EXPORTS = ("pa_reshape_and_cache", "pa_decode", "pa_decode_split", "pa_decode_workspace_bytes",
            "pa_decode_shared_prefix", "pa_decode_shared_prefix_workspace_bytes", "pa_decode_append",
-           "pa_decode_partition_blocks", "pa_prefill", "pa_copy_blocks", "pa_bm_create", "pa_bm_destroy", "pa_bm_num_free_blocks",
+           "pa_decode_partition_blocks", "pa_decode_scratch", "pa_decode_scratch_bytes", "pa_prefill", "pa_copy_blocks", "pa_bm_create", "pa_bm_destroy", "pa_bm_num_free_blocks",
            "pa_bm_block_refcount", "pa_bm_add_sequence", "pa_bm_fork", "pa_bm_free_sequence", "pa_bm_append_slots",
            "pa_bm_block_tables", "pa_bm_shared_prefix", "pa_last_error", "pa_version")
 
@@ -62,6 +62,10 @@ def load(path: str | None = None) -> ctypes.CDLL:
         lib.pa_decode_append.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _f32, _i32, _i32, _i32,
                                          _i32, _i32, _i32, _i64, _i32, _i32, _i32, _f32, _f32, _vp, _sz, _vp]
         lib.pa_decode_append.restype = _i32
+        lib.pa_decode_scratch.argtypes = dec + [_vp]
+        lib.pa_decode_scratch.restype = _i32
+        lib.pa_decode_scratch_bytes.argtypes = []
+        lib.pa_decode_scratch_bytes.restype = _sz
         lib.pa_decode_shared_prefix_workspace_bytes.argtypes = [_i32] * 7
         lib.pa_decode_shared_prefix_workspace_bytes.restype = _sz
         lib.pa_decode_workspace_bytes.argtypes = [_i32] * 7
@@ -204,6 +208,36 @@ def decode(out, q, k_cache, v_cache, block_tables, context_lens, scale: float, n
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens), float(scale),
         num_kv_heads, block_size, S, H, D, M, N, _dtype(q), _dtype(k_cache), _dtype(out), float(k_scale),
         float(v_scale), int(partition_blocks), ws_ptr, ws_bytes, _stream(q, stream)))
+    return out
+
+
+def decode_scratch_bytes() -> int:
+    """Size of the library's fixed scratch array used by :func:`decode_scratch`."""
+    return int(load().pa_decode_scratch_bytes())
+
+
+def decode_scratch(out, q, k_cache, v_cache, block_tables, context_lens, scale: float, num_kv_heads: int,
+                   block_size: int = 16, k_scale: float = 1.0, v_scale: float = 1.0, stream=None) -> torch.Tensor:
+    """:func:`decode` without a workspace: the library's fixed per-GPU scratch array serves instead, so
+    nothing is allocated (pa_decode_scratch). Calls that may overlap on one GPU must be serialised."""
+    lib = load()
+    for t in (out, q, k_cache, v_cache, block_tables, context_lens):
+        _need(t.is_cuda and t.is_contiguous(), "all tensors must be contiguous device tensors")
+    _need(q.dim() == 3 and out.shape == q.shape, "q/out must be [S, H, D] of one shape")
+    _need(k_cache.dim() == 4 and v_cache.shape == k_cache.shape and k_cache.dtype == v_cache.dtype,
+          "caches must be [N, Hkv, B, D] of one shape and dtype")
+    _need(block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32,
+          "block_tables and context_lens must be int32")
+    S, H, D = q.shape
+    _need(block_tables.dim() == 2 and block_tables.shape[0] == S and context_lens.shape == (S,),
+          "block_tables must be [S, M] and context_lens [S]")
+    N, Hkv, B, D2 = k_cache.shape
+    _need(Hkv == num_kv_heads and B == block_size and D2 == D, "cache shape does not match the arguments")
+    with torch.cuda.device(q.device):
+        _check(lib, lib.pa_decode_scratch(
+            _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens), float(scale),
+            num_kv_heads, block_size, S, H, D, block_tables.shape[1], N, _dtype(q), _dtype(k_cache), _dtype(out),
+            float(k_scale), float(v_scale), _stream(q, stream)))
     return out
 
 

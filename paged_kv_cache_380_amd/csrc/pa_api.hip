@@ -5,6 +5,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "pa.h"
@@ -568,6 +569,77 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
   return pa_decode_split(out, q, k_cache, v_cache, block_tables, context_lens, scale, num_kv_heads, block_size,
                          num_seqs, num_heads, head_size, max_blocks_per_seq, num_blocks, q_dtype, cache_dtype,
                          out_dtype, k_scale, v_scale, 0, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// --- pa_decode_scratch: pa_decode without a caller-provided workspace ---------
+//
+// For callers that cannot allocate device memory around a call (code under
+// graph capture, tight serving loops): the workspace is a fixed array in the
+// library's device code, one copy per GPU, held until the process ends.
+
+namespace {
+
+constexpr size_t kScratchBytes = size_t(32) << 20;  // 32 MiB per GPU
+
+// In host code this name only stands for the device array: its address on a
+// device comes from hipGetSymbolAddress, made with that device current.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// Device address of the current device's scratch array in *ptr, looked up
+// once per device (with that device current) and kept. Returns a status.
+int scratch_for_current_device(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "decode_scratch: hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(PA_ERR_UNSUPPORTED, "decode_scratch: device %d is past the %d devices served", dev,
+                kMaxScratchDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(PA_ERR_LAUNCH, "decode_scratch: hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t pa_decode_scratch_bytes(void) { return kScratchBytes; }
+
+int pa_decode_scratch(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens, float scale, int num_kv_heads,
+                      int block_size, int num_seqs, int num_heads, int head_size, int max_blocks_per_seq,
+                      int64_t num_blocks, pa_dtype q_dtype, pa_dtype cache_dtype, pa_dtype out_dtype, float k_scale,
+                      float v_scale, void* stream) {
+  void* ws = nullptr;
+  const int st = scratch_for_current_device(&ws);
+  if (st != PA_OK) return st;
+  // Same choice of schedule as pa_decode with a workspace of kScratchBytes: the
+  // balanced schedule where its need fits, else the partitioned one. Every
+  // element the kernels read from the workspace is written earlier in the same
+  // call, so the array needs no clearing between calls.
+  const int rc = decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, scale, num_kv_heads, block_size,
+                             num_seqs, num_heads, head_size, max_blocks_per_seq, num_blocks, q_dtype, cache_dtype,
+                             out_dtype, k_scale, v_scale, 0, nullptr, 0, ws, kScratchBytes, stream);
+  if (rc == PA_ERR_WORKSPACE) {
+    const std::string why = pa_last_error();
+    return fail(PA_ERR_WORKSPACE, "decode_scratch: these shapes need more than the fixed %zu-byte scratch (%s)",
+                kScratchBytes, why.c_str());
+  }
+  return rc;
 }
 
 }  // extern "C"
