@@ -163,6 +163,32 @@ def summarize_counters(workload: str, fetch_dir: str, write_dir: str, cal_fetch_
     print("\n".join(lines))
 
 
+def summarize_pmc(directory: str, out_path: str, commands: list[str], select: str = ""):
+    """Mean per dispatch of every counter a rocprofv3 --pmc run collected, per kernel (kernels whose name
+    contains ``select``), one row per kernel. Several run directories may be joined with ':'."""
+    per = {}   # kernel -> counter -> dispatch -> value
+    for d in directory.split(":"):
+        for r in _csv_rows(d, "counter_collection.csv"):
+            name = _col(r, "Kernel_Name")
+            if select and select not in name:
+                continue
+            c = per.setdefault(_short(name), {}).setdefault(_col(r, "Counter_Name"), {})
+            key = (d, _col(r, "Dispatch_Id", "Correlation_Id"))
+            c[key] = c.get(key, 0.0) + float(_col(r, "Counter_Value"))
+    if not per:
+        raise SystemExit(f"no counter rows under {directory}")
+    lines = ["# rocprofv3 counters: mean per dispatch over the run, per kernel", "commands:"]
+    lines += [f"  {c}" for c in commands] + [""]
+    for k in sorted(per):
+        lines.append(f"kernel: {k}")
+        for cname in sorted(per[k]):
+            vals = list(per[k][cname].values())
+            lines.append(f"  {cname:<40} {sum(vals) / len(vals):>18.1f}   ({len(vals)} dispatches)")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def cpu_baseline(w, target_seconds: float):
     """The oracle as it stands, on a bounded sample of sequences of the same workload."""
     import numpy as np
@@ -239,6 +265,10 @@ def main():
     ap.add_argument("--summarize-counters", nargs=6,
                     metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR", "COPY_MIB", "OUT"),
                     help="write the HBM-traffic summary of rocprofv3 --pmc runs for --workload and exit")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("DIRS", "OUT"),
+                    help="write the per-kernel mean of every counter of rocprofv3 --pmc runs (DIRS joined by ':') "
+                         "and exit; --select limits the kernels")
+    ap.add_argument("--select", default="", help="kernel-name filter for --summarize-pmc")
     ap.add_argument("--command", action="append", default=[], help="profiling commands recorded in a summary")
     ap.add_argument("--shared-prefix", choices=("auto", "on", "off"), default="auto",
                     help="decode through pa_decode_shared_prefix with the workload's prefix group (auto: when "
@@ -250,6 +280,9 @@ def main():
 
     if args.summarize_stats:
         summarize_stats(*args.summarize_stats)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.command, args.select)
         return
     if args.summarize_counters:
         fd, wd, cfd, cwd, mib, out = args.summarize_counters
@@ -397,6 +430,7 @@ def main():
             "kv_cache_dtype": w.cache_dtype, "seed": w.seed,
             "schedule": "balanced" if balanced_schedule(w, args.partition_blocks) else f"partitions of {pb} blocks",
             "decode_path": os.environ.get("PA_DECODE_PATH", "auto"),
+            "decode_loads": os.environ.get("PA_DECODE_LOADS", "stream"),
             "shared_prefix": [0, w.sharing_seqs, w.shared_blocks] if prefix else None,
             "append": ("in the decode kernel" if one_call and append_fuses(w) else "reshape_and_cache kernel"),
         },

@@ -150,7 +150,8 @@ int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void
  * matrix cores (MFMA); otherwise on the vector ALU. Both give the result above
  * within float32 accumulation error. The environment variable PA_DECODE_PATH
  * (read on every call) forces "valu" or "mfma" (the latter only where it
- * applies), for comparison runs.
+ * applies), for comparison runs; PA_DECODE_LOADS=cached makes the MHA
+ * vector kernel read K/V with cached instead of nontemporal loads (likewise).
  */
 int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
               const int32_t* block_tables, const int32_t* context_lens, float scale,

@@ -61,6 +61,14 @@ bool use_mfma(int q_dtype, int group) {
   return applies && requested_path() != Path::kValu;
 }
 
+// PA_DECODE_LOADS=cached makes the MHA vector kernel read K/V with ordinary
+// cached loads instead of nontemporal ones (read on every call; comparison
+// runs only: the default streaming loads measured faster).
+bool cached_loads_requested() {
+  const char* e = std::getenv("PA_DECODE_LOADS");
+  return e && !std::strcmp(e, "cached");
+}
+
 bool shapes_ok(int num_seqs, int num_heads, int num_kv_heads, int head_size, int max_blocks, int block_size) {
   return num_seqs >= 0 && num_seqs <= 65535 && num_heads >= 1 && num_kv_heads >= 1 &&
          num_heads % num_kv_heads == 0 && (head_size == 64 || head_size == 128) && max_blocks >= 1 &&
@@ -445,6 +453,7 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   a.use_mfma = mfma ? 1 : 0;
   a.group_tile = balanced ? balanced_tile(group) : group_tile;
   a.balanced = balanced ? 1 : 0;
+  a.cached_loads = cached_loads_requested() ? 1 : 0;
   a.ranges = balanced ? (int)ranges : 0;
   a.num_blocks = num_blocks;
   a.max_blocks = max_blocks_per_seq;

@@ -163,7 +163,7 @@ __device__ __forceinline__ float swap_sum16(float a, float b) {
 constexpr int kDppRowRor8 = 0x128;  // lane j <- lane (j - 8) mod 16, i.e. j ^ 8
 constexpr int kDppRowRor4 = 0x124;  // lane j <- lane (j - 4) mod 16
 
-template <int QK, int CK, int D, int GT>
+template <int QK, int CK, int D, int GT, bool kCachedLoads = false>
 __global__ __launch_bounds__(kThreads) void decode_main(const DecodeArgs a) {
   using Geo = TileGeo<CK, D>;
   constexpr int E = Geo::E, LPR = Geo::LPR, RPL = Geo::RPL, NL = Geo::NL;
@@ -260,9 +260,9 @@ __global__ __launch_bounds__(kThreads) void decode_main(const DecodeArgs a) {
     const char* kt = kbase + off;
     const char* vt = vbase + off;
 #pragma unroll
-    for (int i = 0; i < NL; ++i) kr[i] = load_stream(kt + lane_off + i * 1024);
+    for (int i = 0; i < NL; ++i) kr[i] = load_tile_chunk<kCachedLoads>(kt + lane_off + i * 1024);
 #pragma unroll
-    for (int i = 0; i < NL; ++i) vr[i] = load_stream(vt + lane_off + i * 1024);
+    for (int i = 0; i < NL; ++i) vr[i] = load_tile_chunk<kCachedLoads>(vt + lane_off + i * 1024);
   };
 
   auto process = [&](int j, const Tile& t) {
@@ -797,6 +797,11 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)(a.num_kv_heads * (a.group / GT)), (unsigned)a.num_parts, (unsigned)a.num_seqs);
   if constexpr (GT >= 4 && QK != kF32)
     decode_gqa<QK, CK, D, GT><<<grid, dim3(kThreads), 0, stream>>>(a);
+  else if constexpr (GT == 1)
+    if (a.cached_loads)
+      decode_main<QK, CK, D, GT, true><<<grid, dim3(kThreads), 0, stream>>>(a);
+    else
+      decode_main<QK, CK, D, GT><<<grid, dim3(kThreads), 0, stream>>>(a);
   else
     decode_main<QK, CK, D, GT><<<grid, dim3(kThreads), 0, stream>>>(a);
   return hipGetLastError();

@@ -28,6 +28,13 @@ __device__ __forceinline__ uint4 load_stream(const char* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// One 16-byte tile chunk: streaming (nontemporal) by default; an ordinary
+// cached load where a comparison run asks for it.
+template <bool kCached> __device__ __forceinline__ uint4 load_tile_chunk(const char* p) {
+  if constexpr (kCached) return *reinterpret_cast<const uint4*>(p);
+  else return load_stream(p);
+}
+
 __device__ __forceinline__ void store_out(const DecodeArgs& a, int64_t elem, float x) {
   if (a.out_kind == kF32) {
     static_cast<float*>(a.out)[elem] = x;

@@ -55,6 +55,8 @@ struct DecodeArgs {
   int out_kind;           // Kind of out: F32 or the query kind
   int use_mfma;           // 1: matrix-core kernel (16-bit queries, group_tile 4, 8 or 16)
   int balanced;           // 1: balanced schedule (matrix-core kernel only): equal block ranges per wave
+  int cached_loads;       // 1: the MHA vector kernel reads K/V with cached instead of nontemporal loads
+                          //    (comparison runs only, PA_DECODE_LOADS=cached)
   int ranges;             // balanced schedule: number of ranges R (a multiple of 4)
   // Shared-prefix pass (balanced schedule only): groups of consecutive
   // sequences whose block tables start with the same full blocks. The prefix

@@ -231,6 +231,14 @@ def prefix_long_fp8(seed: int = 6) -> Workload:
                  free_fraction=0.10, shared_prefix_blocks=256, sharing_seqs=256, kv_scale=0.05)
 
 
+def mqa_bf16(group: int, seed: int = 7) -> Workload:
+    """Multi-query decode ([vLLM-note] "内核优化": GQA/MQA kernels): one KV head shared by ``group`` query heads;
+    64 sequences x 32768 tokens, head 128, bf16 (1 GiB of K/V, as the Llama-2-7B-shaped batch), pool with no
+    free blocks. Not one of the five reference shapes: it measures large query groups."""
+    return build(f"mqa_g{group}_bf16_b64_ctx32768", [32768] * 64, group, 1, 128, "bf16", seed=seed,
+                 num_blocks=64 * 2048)
+
+
 NAMED = {
     "tiny_fp32": tiny_fp32,
     "llama7b_mha_fp16": llama7b_mha_fp16,
@@ -238,6 +246,9 @@ NAMED = {
     "longctx_bf16": longctx_bf16,
     "prefix_fp8": prefix_fp8,
     "prefix_long_fp8": prefix_long_fp8,
+    "mqa_g32_bf16": lambda seed=7: mqa_bf16(32, seed),
+    "mqa_g64_bf16": lambda seed=7: mqa_bf16(64, seed),
+    "mqa_g128_bf16": lambda seed=7: mqa_bf16(128, seed),
 }
 
 
