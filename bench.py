@@ -549,6 +549,8 @@ def decode_kernel(w) -> str:
     """Name of the decode kernel the library runs for this workload (its selection rule, restated)."""
     group = w.num_heads // w.num_kv_heads
     path = os.environ.get("PA_DECODE_PATH", "auto")
+    if w.dtype in ("f16", "bf16") and group >= 32 and group % 32 == 0 and path != "valu":
+        return "prefill_mfma[decode]"
     if w.dtype in ("f16", "bf16") and group % 4 == 0 and path != "valu":
         return "decode_mfma"
     if w.dtype in ("f16", "bf16") and group % 4 == 0:

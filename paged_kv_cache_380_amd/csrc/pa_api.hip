@@ -26,11 +26,32 @@ bool activation_kind(int k) { return k == PA_DTYPE_F32 || k == PA_DTYPE_F16 || k
 // every unit streaming until the end.
 constexpr int64_t kTargetWorkgroups = 512;
 
+// Groups of 32 and more query heads per KV head (a multiple of 32) decode on
+// the prefill kernel with 16-bit queries: one workgroup per (sequence, KV head,
+// 16 * waves heads, partition), every K/V tile loaded once into LDS for all
+// its heads. Waves per workgroup: 8, 4 or 2 (the most that divides G / 16).
+bool wide_group(int group) { return group >= 32 && group % 32 == 0; }
+int wide_waves(int group) { return (group / 16) % 8 == 0 ? 8 : (group / 16) % 4 == 0 ? 4 : 2; }
+
+// Total waves the wide decode aims at before it splits contexts: two per SIMD.
+constexpr int64_t kWideTargetWaves = 2048;
+
 int choose_partition_blocks(int num_seqs, int num_heads, int num_kv_heads, int max_blocks) {
+  const int group = num_heads / num_kv_heads;
+  if (wide_group(group)) {
+    const int waves = wide_waves(group);
+    const int64_t tiles = (int64_t)num_seqs * num_kv_heads * (group / (16 * waves));
+    int64_t parts = 1;
+    if (tiles > 0 && tiles * waves < kWideTargetWaves) parts = (kWideTargetWaves + tiles * waves - 1) / (tiles * waves);
+    int64_t pb = (max_blocks + parts - 1) / parts;
+    pb = (pb + 3) / 4 * 4;
+    if (pb < 4) pb = 4;
+    if (pb > pa::kMaxPartitionBlocks) pb = pa::kMaxPartitionBlocks;
+    return (int)pb;
+  }
   // Head tiles per KV head as the default kernel for 16-bit queries launches
   // them (the sizing functions see no dtype; any tile count works, this one
   // only steers how far contexts are split).
-  const int group = num_heads / num_kv_heads;
   const int tile = pa::mfma_group_tile(group) ? pa::mfma_group_tile(group) : pa::group_tile_for(group);
   const int64_t tiles = (int64_t)num_seqs * num_kv_heads * (group / tile);
   int64_t parts = 1;
@@ -94,13 +115,10 @@ struct Layout {
 constexpr int kBalancedWaves16 = 1024;
 constexpr int kBalancedWavesFp8 = 2048;
 
-// Query heads per wave in the balanced schedule: 32 (two 16-head sub-tiles
-// sharing every K/V tile) for groups of 64 or more, else the matrix-core
-// tile. Measured at 32 heads over one KV head, two 16-head waves sharing
-// K/V through L2 beat one 32-head wave (its registers leave one wave per
-// SIMD, which cannot overlap its arithmetic with its loads); from 64 heads
-// on, reading K/V once per 32 heads wins.
-int balanced_tile(int group) { return group % 32 == 0 && group >= 64 ? 32 : pa::mfma_group_tile(group); }
+// Query heads per wave in the balanced schedule: the matrix-core tile. The
+// schedule serves groups below 32 and those that are not a multiple of 32
+// (multiples of 32 take the wide decode).
+int balanced_tile(int group) { return wide_group(group) ? 0 : pa::mfma_group_tile(group); }
 
 bool balanced_fits(int num_seqs, int max_blocks) {
   return num_seqs <= pa::kBalancedMaxSeqs && (int64_t)num_seqs * max_blocks <= 0x7fffffffLL;
@@ -400,12 +418,14 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
 
   const int group = num_heads / num_kv_heads;
   const bool mfma = use_mfma(q_dtype, group);
+  const bool wide = mfma && wide_group(group);
   const int group_tile = mfma ? pa::mfma_group_tile(group) : pa::group_tile_for(group);
   // The library's own choice for the matrix-core kernel is the balanced
-  // schedule; an explicit partition length selects the partitioned one.
-  // It needs a workspace; a caller that passes none (or too small a one, as
-  // sized before this schedule existed) gets the partitioned schedule.
-  bool balanced = partition_blocks == 0 && mfma && balanced_fits(num_seqs, max_blocks_per_seq);
+  // schedule (below 32 query heads per KV head); an explicit partition length
+  // selects the partitioned one. It needs a workspace; a caller that passes
+  // none (or too small a one, as sized before this schedule existed) gets the
+  // partitioned schedule.
+  bool balanced = partition_blocks == 0 && mfma && !wide && balanced_fits(num_seqs, max_blocks_per_seq);
   const int64_t ranges = balanced ? balanced_ranges(num_heads, balanced_tile(group), fp8) : 0;
   if (balanced && (!workspace || workspace_bytes < balanced_layout(num_seqs, num_heads, head_size, ranges).total))
     balanced = false;
@@ -430,6 +450,47 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
                   need);
     if (reinterpret_cast<uintptr_t>(workspace) % 256)
       return fail(PA_ERR_WORKSPACE, "decode: workspace must be 256-byte aligned");
+  }
+
+  if (wide) {
+    // Groups of 32 and more (a multiple of 32): the prefill kernel's decode
+    // mode, then decode_reduce for split contexts.
+    pa::PrefillArgs w{};
+    w.out = out;
+    w.q = q;
+    w.k_cache = k_cache;
+    w.v_cache = v_cache;
+    w.block_tables = block_tables;
+    w.context_lens = context_lens;
+    w.query_start_loc = nullptr;
+    const double log2e = 1.4426950408889634;
+    w.qk_scale = (float)((double)scale * log2e * (fp8 ? (double)k_scale : 1.0));
+    w.out_scale = fp8 ? v_scale : 1.0f;
+    w.num_seqs = num_seqs;
+    w.num_heads = num_heads;
+    w.num_kv_heads = num_kv_heads;
+    w.head_size = head_size;
+    w.group = group;
+    w.max_blocks = max_blocks_per_seq;
+    w.num_blocks = num_blocks;
+    w.waves = wide_waves(group);
+    w.row_tiles = group / (16 * w.waves);
+    w.max_query_len = 1;
+    w.out_kind = out_dtype;
+    w.decode = 1;
+    w.part_blocks = L.num_parts > 1 ? pb : 0;
+    w.num_parts = L.num_parts;
+    w.ws_out = L.total ? static_cast<float*>(workspace) : nullptr;
+    w.ws_ml = L.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + L.ml_offset) : nullptr;
+    if (app && !app->fused) {
+      const int rc = reshape_launch(app->key, app->value, app->k_cache, app->v_cache, app->slots, app->slots_int64,
+                                    num_seqs, num_kv_heads, head_size, num_blocks, app->kv_dtype, cache_dtype, k_scale,
+                                    v_scale, stream);
+      if (rc != PA_OK) return rc;
+    }
+    const hipError_t e = pa::launch_decode_wide(w, q_dtype, cache_dtype, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "decode: launch failed: %s", hipGetErrorString(e));
+    return ok();
   }
 
   pa::DecodeArgs a{};

@@ -858,6 +858,10 @@ hipError_t launch_decode(const DecodeArgs& a, int q_kind, int cache_kind, hipStr
     return hipGetLastError();
   }
   if (a.num_parts == 1) return e;
+  return launch_decode_reduce(a, stream);
+}
+
+hipError_t launch_decode_reduce(const DecodeArgs& a, hipStream_t stream) {
   switch (a.head_size) {
     case 64: decode_reduce<64><<<dim3((unsigned)a.num_heads, (unsigned)a.num_seqs), dim3(64), 0, stream>>>(a); break;
     case 128: decode_reduce<128><<<dim3((unsigned)a.num_heads, (unsigned)a.num_seqs), dim3(64), 0, stream>>>(a); break;

@@ -91,6 +91,10 @@ struct DecodeArgs {
 
 // Queues the decode kernel(s) chosen by a.use_mfma, then the partition merge if needed.
 hipError_t launch_decode(const DecodeArgs& a, int q_kind, int cache_kind, hipStream_t stream);
+// The partition merge alone: for every (sequence, head) whose context spans
+// several partitions of a.partition_blocks blocks, merges the a.num_parts
+// slots of ws_out / ws_ml into out (reads out, context_lens, ws_*, sizes).
+hipError_t launch_decode_reduce(const DecodeArgs& a, hipStream_t stream);
 // The matrix-core decode kernel alone (pa_decode_mfma.hip).
 hipError_t launch_decode_mfma(const DecodeArgs& a, int q_kind, int cache_kind, hipStream_t stream);
 // The shared-prefix pass of the matrix-core kernel (a.shared_prefix; 16-bit queries, group 4, 8 or 16).
@@ -120,15 +124,31 @@ struct PrefillArgs {
   int group;
   int max_blocks;
   int64_t num_blocks;
-  int row_tiles;          // workgroups per KV head and sequence: ceil(max_query_len * group / kPrefillRows)
+  int row_tiles;          // workgroups per KV head and sequence: ceil(max_query_len * group / rows per workgroup)
   int max_query_len;      // rows of longer chunks past this many tokens are not computed
   int out_kind;
+  // Decode through the same kernel (groups of 32 and more query heads per KV
+  // head): sequence s has one query, row s of q, and its group's heads are the
+  // rows; query_start_loc is not read. A context longer than part_blocks
+  // blocks is split into partitions (grid z) whose (max, sum, unnormalised
+  // output) go to ws_out / ws_ml in decode_reduce's layout; an empty context
+  // gives zeros.
+  int decode;             // 1: decode mode
+  int waves;              // waves per workgroup (2, 4 or 8; 16 rows each)
+  int part_blocks;        // decode: blocks per partition (0: whole contexts)
+  int num_parts;          // decode: partitions per sequence (grid z)
+  float* ws_out;          // decode, split contexts: [S, H, P, D]
+  float* ws_ml;           // decode, split contexts: [S, H, P, 2]
 };
 
 // Rows ((token, head) pairs of one KV head) per prefill workgroup (16 per wave).
 constexpr int kPrefillRows = 128;
 
 hipError_t launch_prefill(const PrefillArgs& a, int q_kind, int cache_kind, hipStream_t stream);
+
+// Decode for groups of 32 and more query heads per KV head on the prefill
+// kernel (a.decode = 1), then, for split contexts, the partition merge.
+hipError_t launch_decode_wide(const PrefillArgs& a, int q_kind, int cache_kind, hipStream_t stream);
 
 // Copies whole (all KV heads) blocks src[i] -> dst[i] in both caches.
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* src, const int32_t* dst, int num_pairs,

@@ -28,30 +28,38 @@
 //    (on gfx950 the 16x16x32 form issues in the same time as 16x16x16);
 //  * causality is a per-row limit on the key index, applied by selection; a
 //    wave whose rows all end before a block skips its arithmetic.
-// No split over keys is done: a chunk's rows already give many workgroups.
+// No split over keys is done for prefill: a chunk's rows already give many
+// workgroups.
+//
+// Decode mode (groups of 32 and more query heads per KV head, "vLLM" note,
+// section "内核优化": MQA / GQA kernels): the rows are the G query heads of one
+// sequence's single query over one KV head, so every K/V tile loaded into LDS
+// serves all of them; with one wave per 16 or 32 heads reading the tile for
+// itself, each byte would be requested G/16 or G/32 times. The waves per
+// workgroup follow G (2, 4 or 8), and a long context is split into partitions
+// whose partial results decode_reduce merges.
 #include "pa_decode_common.h"
 #include "pa_mfma.h"
 
 namespace pa {
 namespace {
 
-// Waves per workgroup: eight, each with one 16-row tile, so every K/V tile
-// staged in LDS serves 128 rows (measured: 4 waves 392 TFLOP/s, 8 waves 425,
-// 16 waves 286 on 8 x 2048-token GQA prompts).
-constexpr int kPW = kPrefillRows / 16;
-constexpr int kPT = 64 * kPW;
-constexpr int kRT = kPrefillRows / (16 * kPW);  // 16-row tiles per wave
+// Waves per workgroup for prefill: eight, each with one 16-row tile, so every
+// K/V tile staged in LDS serves 128 rows (measured: 4 waves 392 TFLOP/s, 8
+// waves 425, 16 waves 286 on 8 x 2048-token GQA prompts). Decode mode takes
+// 2, 4 or 8 waves, one per 16 heads of the group.
+constexpr int kPrefillWaves = kPrefillRows / 16;
+constexpr int kRT = 1;                              // 16-row tiles per wave
 constexpr int kSB = 2;                              // blocks per step (the P·V operands below pair two)
 static_assert(kSB == 2, "one 16x16x32 P·V product spans two blocks");
 constexpr float kPSlack = 8.0f;
-static_assert(kRT * 16 * kPW == kPrefillRows && (kPW & (kPW - 1)) == 0, "rows split evenly over a power-of-two wave count");
 
-template <int CK, int D> struct PGeo {
+template <int CK, int D, int PW> struct PGeo {
   static constexpr int kBytes = KindBytes<CK>::value;
   static constexpr int kRowBytes = D * kBytes;
   static constexpr int kTileBytes = 16 * kRowBytes;
   static constexpr int NL = kTileBytes / 1024;       // wave-loads of 1 KiB per tile (K or V)
-  static constexpr int NLW = (2 * NL + kPW - 1) / kPW;  // loads per wave per block (K and V together)
+  static constexpr int NLW = (2 * NL + PW - 1) / PW;  // loads per wave per block (K and V together)
   static constexpr int NKB = D / 32;
   static constexpr int NDB = D / 16;
   // LDS row strides of the staged tiles, 16-bit elements. K rows are read
@@ -63,11 +71,13 @@ template <int CK, int D> struct PGeo {
   static constexpr int SV = D + 16;  // V
 };
 
-template <int QK, int CK, int D>
-__global__ __launch_bounds__(kPT) void prefill_mfma(const PrefillArgs a) {
-  using G = PGeo<CK, D>;
+template <int QK, int CK, int D, int PW>
+__global__ __launch_bounds__(64 * PW) void prefill_mfma(const PrefillArgs a) {
+  using G = PGeo<CK, D, PW>;
   constexpr int NL = G::NL, NLW = G::NLW, NKB = G::NKB, NDB = G::NDB, S = G::S, SV = G::SV;
+  constexpr int kRows = 16 * PW;  // rows per workgroup
   static_assert(QK == kF16 || QK == kBF16, "16-bit queries");
+  static_assert(PW == 2 || PW == 4 || PW == 8, "2, 4 or 8 waves");
 
   __shared__ __align__(16) uint16_t s_k[2][kSB][16 * S];
   __shared__ __align__(16) uint16_t s_v[2][kSB][16 * SV];
@@ -75,23 +85,43 @@ __global__ __launch_bounds__(kPT) void prefill_mfma(const PrefillArgs a) {
   const int kvh = blockIdx.x / a.row_tiles;
   const int rt = blockIdx.x - kvh * a.row_tiles;
   const int seq = blockIdx.y;
+  const int part = blockIdx.z;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15;
   const int g = lane >> 4;
 
-  const int q0 = a.query_start_loc[seq];
   const int ctx = min(a.context_lens[seq], a.max_blocks * 16);
-  const int qlen = min(a.query_start_loc[seq + 1] - q0, ctx);  // the chunk: positions ctx - qlen .. ctx - 1
+  // Prefill: the chunk is positions ctx - qlen .. ctx - 1. Decode: one query, row seq of q.
+  const int q0 = a.decode ? seq : a.query_start_loc[seq];
+  const int qlen = a.decode ? (ctx > 0 ? 1 : 0) : min(a.query_start_loc[seq + 1] - q0, ctx);
   const int rows = min(qlen, a.max_query_len) * a.group;        // rows computed (the grid covers max_query_len)
-  const int row0 = rt * kPrefillRows;
+  const int row0 = rt * kRows;
+  if (a.decode && ctx <= 0) {  // nothing to attend: zeros (written once, by partition 0)
+    if (part == 0)
+      for (int idx = tid; idx < kRows * D; idx += 64 * PW) {
+        const int r = row0 + idx / D;
+        if (r < a.group) {
+          const int64_t e = ((int64_t)seq * a.num_heads + kvh * a.group + r) * D + idx % D;
+          if (a.out_kind == kF32) static_cast<float*>(a.out)[e] = 0.f;
+          else static_cast<uint16_t*>(a.out)[e] = 0;
+        }
+      }
+    return;
+  }
   if (row0 >= rows) return;
-  const int last_row = min(row0 + kPrefillRows, rows) - 1;
-  const int nblk = (ctx - qlen + last_row / a.group + 1 + 15) >> 4;  // blocks up to the last row's position
+  const int last_row = min(row0 + kRows, rows) - 1;
+  const int nblk_all = (ctx - qlen + last_row / a.group + 1 + 15) >> 4;  // blocks up to the last row's position
+  // Decode partitions: blocks [blk0, nblk) of the context (the whole of it when not split).
+  const int blk0 = a.part_blocks ? part * a.part_blocks : 0;
+  const int nblk = a.part_blocks ? min(nblk_all, blk0 + a.part_blocks) : nblk_all;
+  if (blk0 >= nblk) return;
+  const int seq_parts = a.part_blocks ? (nblk_all + a.part_blocks - 1) / a.part_blocks : 1;
 
   // This lane's S columns: row n of each of the wave's 16-row tiles.
   const int wrow0 = row0 + wave * 16 * kRT;
+  static_assert(kRT == 1, "one 16-row tile per wave");
   int my_limit[kRT];  // keys visible to the row (0 for rows past the chunk)
   uint32_t qf[kRT][NKB][4];
 #pragma unroll
@@ -121,7 +151,7 @@ __global__ __launch_bounds__(kPT) void prefill_mfma(const PrefillArgs a) {
   const char* kbase = static_cast<const char*>(a.k_cache) + (int64_t)kvh * G::kTileBytes;
   const char* vbase = static_cast<const char*>(a.v_cache) + (int64_t)kvh * G::kTileBytes;
 
-  // The tiles of step j (blocks kSB*j .. kSB*j + kSB - 1), as this wave's
+  // The tiles of step j (blocks blk0 + kSB*j .. blk0 + kSB*j + kSB - 1), as this wave's
   // share of the 2*NL wave-loads per block (K first, then V), into register
   // buffer rb; loads run two steps ahead of the arithmetic. The loads are
   // unconditional, so that the compiler's wait before staging a step counts
@@ -132,14 +162,14 @@ __global__ __launch_bounds__(kPT) void prefill_mfma(const PrefillArgs a) {
   auto issue = [&](int j, int rb) {
 #pragma unroll
     for (int p = 0; p < kSB; ++p) {
-      const int blk = min(kSB * j + p, nblk - 1);
+      const int blk = min(blk0 + kSB * j + p, nblk - 1);
       // A scalar load (the table is read-only here): waiting for it does not
       // wait for the vector loads of the steps in flight.
       const int phys = ((const __attribute__((address_space(4))) int32_t*)bt)[blk];
       const int64_t off = ((uint32_t)phys < (uint64_t)a.num_blocks ? phys : 0) * blk_stride;
 #pragma unroll
       for (int u = 0; u < NLW; ++u) {
-        const int L = (wave & (kPW - 1)) + u * kPW;  // wave < kPW, stated for the compiler
+        const int L = (wave & (PW - 1)) + u * PW;  // wave < PW, stated for the compiler
         if (L < 2 * NL) {
           const char* base = L < NL ? kbase : vbase;
           pre[rb][p][u] = load_stream(base + off + (L % NL) * 1024 + lane * 16);
@@ -150,7 +180,7 @@ __global__ __launch_bounds__(kPT) void prefill_mfma(const PrefillArgs a) {
   auto stage = [&](int j, int buf, int rb) {
 #pragma unroll
     for (int p = 0; p < kSB; ++p) {
-      const int blk = kSB * j + p;
+      const int blk = blk0 + kSB * j + p;
       // Blocks before the last needed one lie wholly inside the context and
       // are stored as loaded; the last one (rows past the context may hold
       // anything: V rows there become zero, as a zero weight times NaN would
@@ -159,7 +189,7 @@ __global__ __launch_bounds__(kPT) void prefill_mfma(const PrefillArgs a) {
       const bool inside = blk + 1 < nblk;
 #pragma unroll
       for (int u = 0; u < NLW; ++u) {
-        const int L = (wave & (kPW - 1)) + u * kPW;  // wave < kPW, stated for the compiler
+        const int L = (wave & (PW - 1)) + u * PW;  // wave < PW, stated for the compiler
         if (L < 2 * NL) {
           const bool is_v = L >= NL;
           const int byte = (L % NL) * 1024 + lane * 16;
@@ -201,7 +231,7 @@ __global__ __launch_bounds__(kPT) void prefill_mfma(const PrefillArgs a) {
   const float qk_scale = a.qk_scale;
 
   auto compute = [&](int j, int buf) {
-    const int key0 = kSB * 16 * j;  // first key of the step
+    const int key0 = (blk0 + kSB * j) * 16;  // first key of the step
     if (key0 >= wave_limit) return;  // every row of this wave ends before this step
     f32x4_t s[kRT][kSB];
 #pragma unroll
@@ -277,7 +307,7 @@ __global__ __launch_bounds__(kPT) void prefill_mfma(const PrefillArgs a) {
     }
   };
 
-  const int nsteps = (nblk + kSB - 1) / kSB;
+  const int nsteps = (nblk - blk0 + kSB - 1) / kSB;
   issue(0, 0);
   issue(1, 1);
   __builtin_amdgcn_sched_barrier(0);
@@ -302,12 +332,31 @@ __global__ __launch_bounds__(kPT) void prefill_mfma(const PrefillArgs a) {
   }
 
   // Normalise and write this wave's rows: lane (n, g) holds rows 4g + i of
-  // each tile, column 16 db + n.
+  // each tile, column 16 db + n. A partition of a split decode context
+  // leaves its running max (log2 units), sum and unnormalised output instead.
 #pragma unroll
   for (int t = 0; t < kRT; ++t) {
     float ls = lsum[t];
     ls += __shfl_xor(ls, 16, 64);
     ls += __shfl_xor(ls, 32, 64);
+    if (seq_parts > 1) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = wrow0 + t * 16 + 4 * g + i;  // decode: the row is the head within the group
+        const float L = __shfl(ls, 4 * g + i, 64);
+        const float M = __shfl(mref[t], 4 * g + i, 64);
+        if (r < rows) {
+          const int64_t pi = ((int64_t)seq * a.num_heads + kvh * a.group + r) * a.num_parts + part;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) a.ws_out[pi * D + db * 16 + n] = acc[t][db][i] * a.out_scale;
+          if (n == 0) {
+            a.ws_ml[2 * pi] = M;
+            a.ws_ml[2 * pi + 1] = L;
+          }
+        }
+      }
+      continue;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = wrow0 + t * 16 + 4 * g + i;
@@ -330,15 +379,26 @@ __global__ __launch_bounds__(kPT) void prefill_mfma(const PrefillArgs a) {
   }
 }
 
-template <int QK, int CK>
-hipError_t launch_d(const PrefillArgs& a, hipStream_t stream) {
-  const dim3 grid((unsigned)(a.row_tiles * a.num_kv_heads), (unsigned)a.num_seqs);
-  switch (a.head_size) {
-    case 64: prefill_mfma<QK, CK, 64><<<grid, dim3(kPT), 0, stream>>>(a); break;
-    case 128: prefill_mfma<QK, CK, 128><<<grid, dim3(kPT), 0, stream>>>(a); break;
+template <int QK, int CK, int D>
+hipError_t launch_w(const PrefillArgs& a, hipStream_t stream) {
+  const dim3 grid((unsigned)(a.row_tiles * a.num_kv_heads), (unsigned)a.num_seqs,
+                  (unsigned)(a.decode && a.part_blocks ? a.num_parts : 1));
+  switch (a.decode ? a.waves : kPrefillWaves) {
+    case 2: prefill_mfma<QK, CK, D, 2><<<grid, dim3(64 * 2), 0, stream>>>(a); break;
+    case 4: prefill_mfma<QK, CK, D, 4><<<grid, dim3(64 * 4), 0, stream>>>(a); break;
+    case 8: prefill_mfma<QK, CK, D, 8><<<grid, dim3(64 * 8), 0, stream>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <int QK, int CK>
+hipError_t launch_d(const PrefillArgs& a, hipStream_t stream) {
+  switch (a.head_size) {
+    case 64: return launch_w<QK, CK, 64>(a, stream);
+    case 128: return launch_w<QK, CK, 128>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
@@ -351,6 +411,25 @@ hipError_t launch_prefill(const PrefillArgs& a, int q_kind, int cache_kind, hipS
     case kBF16 * 4 + kFP8: return launch_d<kBF16, kFP8>(a, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_decode_wide(const PrefillArgs& a, int q_kind, int cache_kind, hipStream_t stream) {
+  const hipError_t e = launch_prefill(a, q_kind, cache_kind, stream);
+  if (e != hipSuccess || !a.part_blocks || a.num_parts <= 1) return e;
+  // Merge the partitions (the decode path's merge kernel, same workspace layout).
+  DecodeArgs r{};
+  r.out = a.out;
+  r.context_lens = a.context_lens;
+  r.ws_out = a.ws_out;
+  r.ws_ml = a.ws_ml;
+  r.num_seqs = a.num_seqs;
+  r.num_heads = a.num_heads;
+  r.head_size = a.head_size;
+  r.max_blocks = a.max_blocks;
+  r.partition_blocks = a.part_blocks;
+  r.num_parts = a.num_parts;
+  r.out_kind = a.out_kind;
+  return launch_decode_reduce(r, stream);
 }
 
 }  // namespace pa

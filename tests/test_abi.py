@@ -145,13 +145,13 @@ def test_balanced_workspace_bytes(lib):
     ml_off = (out_bytes + 255) // 256 * 256
     pref_off = (ml_off + rows * 2 * 4 + 255) // 256 * 256
     assert lib.pa_decode_workspace_bytes(S, H, Hkv, D, M, 16, 0) == pref_off + (S + 1) * 4
-    # 64 query heads over one KV head: 32-head tiles, two columns, R = 512 ranges
-    # (a 32-head tile runs one wave per SIMD, so no FP8 doubling)
-    rows = 64 * (S + 512)
+    # 64 query heads over one KV head: the wide decode (workgroups of 4 waves x 16 heads, one per sequence),
+    # 64 x 4 = 256 waves, split into 2048 / 256 = 8 partitions of 32 blocks: [S, H, P, D] + [S, H, P, 2] floats
+    P = 8
+    rows = S * 64 * P
     out_bytes = rows * D * 4
-    ml_off = (out_bytes + 255) // 256 * 256
-    pref_off = (ml_off + rows * 2 * 4 + 255) // 256 * 256
-    assert lib.pa_decode_workspace_bytes(S, 64, 1, D, M, 16, 0) == pref_off + (S + 1) * 4
+    assert binding.decode_partition_blocks(S, 64, 1, D, M) == M // P
+    assert lib.pa_decode_workspace_bytes(S, 64, 1, D, M, 16, 0) == (out_bytes + 255) // 256 * 256 + rows * 2 * 4
     # no head tile of 4 (group 6): only the partitioned schedule can run
     assert lib.pa_decode_workspace_bytes(S, 48, 8, D, M, 16, 0) == 0
     # past the largest balanced batch: only the partitioned schedule
