@@ -33,16 +33,20 @@ constexpr int64_t kTargetWorkgroups = 512;
 bool wide_group(int group) { return group >= 32 && group % 32 == 0; }
 int wide_waves(int group) { return (group / 16) % 8 == 0 ? 8 : (group / 16) % 4 == 0 ? 4 : 2; }
 
-// Total waves the wide decode aims at before it splits contexts: two per SIMD.
-constexpr int64_t kWideTargetWaves = 2048;
+// Workgroups the wide decode aims at before it splits contexts: two per
+// compute unit, and for 2-wave workgroups four (measured on 64 sequences of
+// 32768 tokens over one KV head: 8-wave workgroups at two per unit 0.274 ms
+// against 0.306 ms at one; 2- and 4-wave workgroups slower beyond these).
+int64_t wide_target_workgroups(int waves) { return waves == 2 ? 1024 : 512; }
 
 int choose_partition_blocks(int num_seqs, int num_heads, int num_kv_heads, int max_blocks) {
   const int group = num_heads / num_kv_heads;
   if (wide_group(group)) {
     const int waves = wide_waves(group);
     const int64_t tiles = (int64_t)num_seqs * num_kv_heads * (group / (16 * waves));
+    const int64_t target = wide_target_workgroups(waves);
     int64_t parts = 1;
-    if (tiles > 0 && tiles * waves < kWideTargetWaves) parts = (kWideTargetWaves + tiles * waves - 1) / (tiles * waves);
+    if (tiles > 0 && tiles < target) parts = (target + tiles - 1) / tiles;
     int64_t pb = (max_blocks + parts - 1) / parts;
     pb = (pb + 3) / 4 * 4;
     if (pb < 4) pb = 4;

@@ -83,7 +83,9 @@ __global__ __launch_bounds__(64 * PW) void prefill_mfma(const PrefillArgs a) {
   __shared__ __align__(16) uint16_t s_v[2][kSB][16 * SV];
 
   const int kvh = blockIdx.x / a.row_tiles;
-  const int rt = blockIdx.x - kvh * a.row_tiles;
+  // Causal prefill: later rows see more keys, so the row tiles are dispatched
+  // last-first (the longest workgroups start earliest).
+  const int rt = a.decode ? blockIdx.x - kvh * a.row_tiles : a.row_tiles - 1 - (blockIdx.x - kvh * a.row_tiles);
   const int seq = blockIdx.y;
   const int part = blockIdx.z;
   const int tid = threadIdx.x;
@@ -142,9 +144,24 @@ __global__ __launch_bounds__(64 * PW) void prefill_mfma(const PrefillArgs a) {
       qf[t][b][3] = v.w;
     }
   }
-  // The wave's largest limit (its last valid row): blocks at or past it are skipped.
+  // The wave's largest limit (its last valid row): blocks at or past it are
+  // skipped. Its smallest (its first row): steps wholly below it need no mask.
   const int wave_last = min(wrow0 + 16 * kRT - 1, rows - 1);
   const int wave_limit = wrow0 < rows ? ctx - qlen + wave_last / a.group + 1 : 0;
+  const int wave_first_limit = wrow0 < rows ? ctx - qlen + wrow0 / a.group + 1 : 0;
+  // Scores are scaled inside the exponent, exp2(s * c - m), which needs c >= 0:
+  // a negative scale is moved into q (its sign flipped, exactly), and a zero
+  // one is raised to 1e-30 (weights then equal to within float32 rounding, and
+  // -inf scores stay -inf).
+  if (a.qk_scale < 0.f) {
+#pragma unroll
+    for (int t = 0; t < kRT; ++t)
+#pragma unroll
+      for (int b = 0; b < NKB; ++b)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) qf[t][b][w] ^= 0x80008000u;
+  }
+  const float qk_c = fmaxf(fabsf(a.qk_scale), 1e-30f);
 
   const int32_t* bt = a.block_tables + (int64_t)seq * a.max_blocks;
   const int64_t blk_stride = (int64_t)a.num_kv_heads * G::kTileBytes;
@@ -228,8 +245,6 @@ __global__ __launch_bounds__(64 * PW) void prefill_mfma(const PrefillArgs a) {
     mref[t] = kNegInf;
     lsum[t] = 0.f;
   }
-  const float qk_scale = a.qk_scale;
-
   auto compute = [&](int j, int buf) {
     const int key0 = (blk0 + kSB * j) * 16;  // first key of the step
     if (key0 >= wave_limit) return;  // every row of this wave ends before this step
@@ -250,19 +265,32 @@ __global__ __launch_bounds__(64 * PW) void prefill_mfma(const PrefillArgs a) {
       }
     }
     uint32_t ph[kRT][kSB][2], pl[kRT][kSB][2];
+    // Steps wholly below every row's limit need no mask (a wave-uniform choice).
+    const bool full = key0 + kSB * 16 <= wave_first_limit;
 #pragma unroll
     for (int t = 0; t < kRT; ++t) {
-      float x[kSB][4];
+      float x[kSB][4];  // unscaled scores
       float bm = kNegInf;
+      if (full) {
 #pragma unroll
-      for (int p = 0; p < kSB; ++p)
+        for (int p = 0; p < kSB; ++p)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          x[p][i] = s[t][p][i] * qk_scale;
-          // causal limit (and rows past the chunk), by selection
-          if (key0 + 16 * p + 4 * g + i >= my_limit[t]) x[p][i] = kNegInf;
-          bm = fmaxf(bm, x[p][i]);
-        }
+          for (int i = 0; i < 4; ++i) {
+            x[p][i] = s[t][p][i];
+            bm = fmaxf(bm, x[p][i]);
+          }
+      } else {
+#pragma unroll
+        for (int p = 0; p < kSB; ++p)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            x[p][i] = s[t][p][i];
+            // causal limit (and rows past the chunk), by selection
+            if (key0 + 16 * p + 4 * g + i >= my_limit[t]) x[p][i] = kNegInf;
+            bm = fmaxf(bm, x[p][i]);
+          }
+      }
+      bm *= qk_c;  // the step's largest logit (c >= 0 keeps the order)
       if (__builtin_amdgcn_ballot_w64(bm > mref[t] + kPSlack) != 0) {
         float bmx = fmaxf(bm, __shfl_xor(bm, 16, 64));
         bmx = fmaxf(bmx, __shfl_xor(bmx, 32, 64));
@@ -283,7 +311,7 @@ __global__ __launch_bounds__(64 * PW) void prefill_mfma(const PrefillArgs a) {
         float pr[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          pr[i] = fast_exp2(x[p][i] - ms);
+          pr[i] = fast_exp2(__builtin_fmaf(x[p][i], qk_c, -ms));
           lsum[t] += pr[i];
         }
         ph[t][p][0] = pack2<QK>(pr[0], pr[1]);

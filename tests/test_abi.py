@@ -146,7 +146,7 @@ def test_balanced_workspace_bytes(lib):
     pref_off = (ml_off + rows * 2 * 4 + 255) // 256 * 256
     assert lib.pa_decode_workspace_bytes(S, H, Hkv, D, M, 16, 0) == pref_off + (S + 1) * 4
     # 64 query heads over one KV head: the wide decode (workgroups of 4 waves x 16 heads, one per sequence),
-    # 64 x 4 = 256 waves, split into 2048 / 256 = 8 partitions of 32 blocks: [S, H, P, D] + [S, H, P, 2] floats
+    # 64 workgroups, split into 512 / 64 = 8 partitions of 32 blocks: [S, H, P, D] + [S, H, P, 2] floats
     P = 8
     rows = S * 64 * P
     out_bytes = rows * D * 4
