@@ -675,6 +675,17 @@ __global__ __launch_bounds__(64) void decode_bal_reduce(const DecodeArgs a) {
   const int64_t T = a.ws_pref[a.num_seqs];
   const int64_t sh = (int64_t)seq * a.num_heads + h;
   const int shb = a.shared_prefix ? a.ws_shared[seq] : 0;  // shared blocks, merged from the prefix pass
+  // The prefix pass's first part (its only one for prefixes of at most
+  // kPrefixPartBlocks blocks), loaded in the same round as the indices above
+  // (its address does not depend on them; the slot exists for every sequence).
+  float pm0 = kNegInf, pl0 = 0.f, po0[D / 64];
+  if (a.shared_prefix) {
+    const int64_t p0 = ((int64_t)h * a.num_seqs + seq) * a.prefix_parts;
+    pm0 = a.ws_sh_ml[2 * p0];
+    pl0 = a.ws_sh_ml[2 * p0 + 1];
+#pragma unroll
+    for (int k = 0; k < D / 64; ++k) po0[k] = a.ws_sh_out[p0 * D + lane + 64 * k];
+  }
   if (ps >= pe && shb <= 0) {
 #pragma unroll
     for (int k = 0; k < D / 64; ++k) store_out(a, sh * D + lane + 64 * k, 0.f);
@@ -772,16 +783,20 @@ __global__ __launch_bounds__(64) void decode_bal_reduce(const DecodeArgs a) {
     const int64_t p0 = ((int64_t)h * a.num_seqs + seq) * a.prefix_parts;
     const float* pml = a.ws_sh_ml + 2 * p0;
     const float* po = a.ws_sh_out + p0 * D;
-    float Mp = kNegInf;
-    for (int i = lane; i < np; i += 64) Mp = fmaxf(Mp, pml[2 * i]);
+    float Mp = pm0;
+    for (int i = 1 + lane; i < np; i += 64) Mp = fmaxf(Mp, pml[2 * i]);
+    if (np > 1) {
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) Mp = fmaxf(Mp, __shfl_xor(Mp, off, 64));
+      for (int off = 32; off >= 1; off >>= 1) Mp = fmaxf(Mp, __shfl_xor(Mp, off, 64));
+    }
     const float Mn = fmaxf(M, Mp);
     const float fo = M == kNegInf ? 0.f : fast_exp2(M - Mn);
     L *= fo;
+    const float f0 = fast_exp2(pm0 - Mn);
+    L += pl0 * f0;
 #pragma unroll
-    for (int k = 0; k < D / 64; ++k) O[k] *= fo;
-    for (int i = 0; i < np; ++i) {
+    for (int k = 0; k < D / 64; ++k) O[k] = O[k] * fo + po0[k] * f0;
+    for (int i = 1; i < np; ++i) {
       const float f = fast_exp2(pml[2 * i] - Mn);
       L += pml[2 * i + 1] * f;
 #pragma unroll
