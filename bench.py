@@ -135,7 +135,7 @@ def summarize_counters(workload: str, fetch_dir: str, write_dir: str, cal_fetch_
     """HBM bytes per decode call (all its kernels: prefix pass, main kernel, merge): FETCH_SIZE and
     WRITE_SIZE (KiB) scaled by what they read for a plain copy."""
     from paged_kv_cache_380_amd import workloads as wl
-    is_decode = lambda n: "decode_" in n
+    is_decode = lambda n: "decode_" in n or "prefill_mfma" in n  # groups of 32+ decode on the prefill kernel
     is_copy = lambda n: "copy" in n.lower()
     fetch, nf, kname = _counter_means(fetch_dir, "FETCH_SIZE", is_decode)
     write, nw, _ = _counter_means(write_dir, "WRITE_SIZE", is_decode)
