@@ -629,28 +629,62 @@ __global__ __launch_bounds__(kThreads) void decode_gqa(const DecodeArgs a) {
 }
 
 // Merge the partitions of every (sequence, head) whose context spans several.
+// Up to 64 partitions take one round of loads: lane p reads partition p's
+// max and sum, every lane its columns of the first kPre partitions' outputs;
+// the weights are then shared by lane reads (partitions past kPre, and past
+// 64, are read in further rounds). The merge order is fixed: deterministic.
 template <int D>
 __global__ __launch_bounds__(64) void decode_reduce(const DecodeArgs a) {
+  constexpr int kPre = 16;
   const int h = blockIdx.x;
   const int seq = blockIdx.y;
   const int lane = threadIdx.x;
   const int ctx = context_len(a, seq);
   const int seq_parts = (((ctx + 15) >> 4) + a.partition_blocks - 1) / a.partition_blocks;
-  if (seq_parts <= 1) return;  // written directly by decode_main
+  if (seq_parts <= 1) return;  // written directly by the decode kernel
   const int64_t base = ((int64_t)seq * a.num_heads + h) * a.num_parts;
   const float* ml = a.ws_ml + 2 * base;
   const float* o = a.ws_out + base * D;
-  float M = kNegInf;
-  for (int p = 0; p < seq_parts; ++p) M = fmaxf(M, ml[2 * p]);
-  float L = 0.f;
   float O[D / 64];
 #pragma unroll
   for (int k = 0; k < D / 64; ++k) O[k] = 0.f;
-  for (int p = 0; p < seq_parts; ++p) {
-    const float f = fast_exp2(ml[2 * p] - M);
-    L += ml[2 * p + 1] * f;
+  float M = kNegInf, L = 0.f;
+  if (seq_parts <= 64) {
+    float ov[kPre][D / 64];
 #pragma unroll
-    for (int k = 0; k < D / 64; ++k) O[k] += o[(int64_t)p * D + lane + 64 * k] * f;
+    for (int j = 0; j < kPre; ++j)
+#pragma unroll
+      for (int k = 0; k < D / 64; ++k) ov[j][k] = j < seq_parts ? o[(int64_t)j * D + lane + 64 * k] : 0.f;
+    const bool mine = lane < seq_parts;
+    const float m = mine ? ml[2 * lane] : kNegInf;
+    const float l = mine ? ml[2 * lane + 1] : 0.f;
+    M = m;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+    const float f = mine ? fast_exp2(m - M) : 0.f;
+    L = l * f;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off, 64);
+#pragma unroll
+    for (int j = 0; j < kPre; ++j) {
+      const float fj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), j));
+#pragma unroll
+      for (int k = 0; k < D / 64; ++k) O[k] += ov[j][k] * fj;
+    }
+#pragma unroll 4
+    for (int j = kPre; j < seq_parts; ++j) {
+      const float fj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), j));
+#pragma unroll
+      for (int k = 0; k < D / 64; ++k) O[k] += o[(int64_t)j * D + lane + 64 * k] * fj;
+    }
+  } else {
+    for (int p = 0; p < seq_parts; ++p) M = fmaxf(M, ml[2 * p]);
+    for (int p = 0; p < seq_parts; ++p) {
+      const float f = fast_exp2(ml[2 * p] - M);
+      L += ml[2 * p + 1] * f;
+#pragma unroll
+      for (int k = 0; k < D / 64; ++k) O[k] += o[(int64_t)p * D + lane + 64 * k] * f;
+    }
   }
   const int64_t sh = (int64_t)seq * a.num_heads + h;
 #pragma unroll
