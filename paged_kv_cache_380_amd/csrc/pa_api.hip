@@ -32,6 +32,17 @@ constexpr int64_t kTargetWorkgroups = 512;
 // its heads. Waves per workgroup: 8, 4 or 2 (the most that divides G / 16).
 bool wide_group(int group) { return group >= 32 && group % 32 == 0; }
 int wide_waves(int group) { return (group / 16) % 8 == 0 ? 8 : (group / 16) % 4 == 0 ? 4 : 2; }
+// Workgroup shape of the wide decode: 128 heads go to 4 waves of two 16-head
+// tiles each rather than 8 waves of one (each tile read from LDS once per 32
+// heads; measured 0.261 against 0.267 ms on 64 x 32768 tokens at G = 128).
+void wide_shape(int group, int& waves, int& wave_tiles) {
+  waves = wide_waves(group);
+  wave_tiles = 1;
+  if (waves == 8) {
+    waves = 4;
+    wave_tiles = 2;
+  }
+}
 
 // Workgroups the wide decode aims at before it splits contexts: two per
 // compute unit, and for 2-wave workgroups four (measured on 64 sequences of
@@ -42,8 +53,9 @@ int64_t wide_target_workgroups(int waves) { return waves == 2 ? 1024 : 512; }
 int choose_partition_blocks(int num_seqs, int num_heads, int num_kv_heads, int max_blocks) {
   const int group = num_heads / num_kv_heads;
   if (wide_group(group)) {
-    const int waves = wide_waves(group);
-    const int64_t tiles = (int64_t)num_seqs * num_kv_heads * (group / (16 * waves));
+    int waves, wave_tiles;
+    wide_shape(group, waves, wave_tiles);
+    const int64_t tiles = (int64_t)num_seqs * num_kv_heads * (group / (16 * waves * wave_tiles));
     const int64_t target = wide_target_workgroups(waves);
     int64_t parts = 1;
     if (tiles > 0 && tiles < target) parts = (target + tiles - 1) / tiles;
@@ -315,6 +327,8 @@ int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cach
   a.row_tiles = (int)row_tiles;
   a.max_query_len = max_query_len;
   a.out_kind = out_dtype;
+  a.waves = pa::kPrefillRows / 16;
+  a.wave_tiles = 1;
   const hipError_t e = pa::launch_prefill(a, q_dtype, cache_dtype, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "prefill: launch failed: %s", hipGetErrorString(e));
   return ok();
@@ -477,8 +491,8 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
     w.group = group;
     w.max_blocks = max_blocks_per_seq;
     w.num_blocks = num_blocks;
-    w.waves = wide_waves(group);
-    w.row_tiles = group / (16 * w.waves);
+    wide_shape(group, w.waves, w.wave_tiles);
+    w.row_tiles = group / (16 * w.waves * w.wave_tiles);
     w.max_query_len = 1;
     w.out_kind = out_dtype;
     w.decode = 1;

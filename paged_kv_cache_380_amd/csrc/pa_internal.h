@@ -134,7 +134,8 @@ struct PrefillArgs {
   // output) go to ws_out / ws_ml in decode_reduce's layout; an empty context
   // gives zeros.
   int decode;             // 1: decode mode
-  int waves;              // waves per workgroup (2, 4 or 8; 16 rows each)
+  int waves;              // waves per workgroup (2, 4 or 8)
+  int wave_tiles;         // 16-row tiles per wave (1; 2 with 4 waves)
   int part_blocks;        // decode: blocks per partition (0: whole contexts)
   int num_parts;          // decode: partitions per sequence (grid z)
   float* ws_out;          // decode, split contexts: [S, H, P, D]

@@ -35,9 +35,10 @@
 // section "内核优化": MQA / GQA kernels): the rows are the G query heads of one
 // sequence's single query over one KV head, so every K/V tile loaded into LDS
 // serves all of them; with one wave per 16 or 32 heads reading the tile for
-// itself, each byte would be requested G/16 or G/32 times. The waves per
-// workgroup follow G (2, 4 or 8), and a long context is split into partitions
-// whose partial results decode_reduce merges.
+// itself, each byte would be requested G/16 or G/32 times. The workgroup
+// follows G (2 or 4 waves of 16 heads; from 128 heads on, 4 waves of two
+// 16-head tiles), and a long context is split into partitions whose partial
+// results decode_reduce merges.
 #include "pa_decode_common.h"
 #include "pa_mfma.h"
 
@@ -49,7 +50,6 @@ namespace {
 // waves 425, 16 waves 286 on 8 x 2048-token GQA prompts). Decode mode takes
 // 2, 4 or 8 waves, one per 16 heads of the group.
 constexpr int kPrefillWaves = kPrefillRows / 16;
-constexpr int kRT = 1;                              // 16-row tiles per wave
 constexpr int kSB = 2;                              // blocks per step (the P·V operands below pair two)
 static_assert(kSB == 2, "one 16x16x32 P·V product spans two blocks");
 constexpr float kPSlack = 8.0f;
@@ -71,13 +71,14 @@ template <int CK, int D, int PW> struct PGeo {
   static constexpr int SV = D + 16;  // V
 };
 
-template <int QK, int CK, int D, int PW>
+template <int QK, int CK, int D, int PW, int kRT = 1>
 __global__ __launch_bounds__(64 * PW) void prefill_mfma(const PrefillArgs a) {
   using G = PGeo<CK, D, PW>;
   constexpr int NL = G::NL, NLW = G::NLW, NKB = G::NKB, NDB = G::NDB, S = G::S, SV = G::SV;
-  constexpr int kRows = 16 * PW;  // rows per workgroup
+  constexpr int kRows = 16 * kRT * PW;  // rows per workgroup (kRT 16-row tiles per wave)
   static_assert(QK == kF16 || QK == kBF16, "16-bit queries");
   static_assert(PW == 2 || PW == 4 || PW == 8, "2, 4 or 8 waves");
+  static_assert(kRT == 1 || kRT == 2, "one or two 16-row tiles per wave");
 
   __shared__ __align__(16) uint16_t s_k[2][kSB][16 * S];
   __shared__ __align__(16) uint16_t s_v[2][kSB][16 * SV];
@@ -123,7 +124,6 @@ __global__ __launch_bounds__(64 * PW) void prefill_mfma(const PrefillArgs a) {
 
   // This lane's S columns: row n of each of the wave's 16-row tiles.
   const int wrow0 = row0 + wave * 16 * kRT;
-  static_assert(kRT == 1, "one 16-row tile per wave");
   int my_limit[kRT];  // keys visible to the row (0 for rows past the chunk)
   uint32_t qf[kRT][NKB][4];
 #pragma unroll
@@ -411,10 +411,11 @@ template <int QK, int CK, int D>
 hipError_t launch_w(const PrefillArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)(a.row_tiles * a.num_kv_heads), (unsigned)a.num_seqs,
                   (unsigned)(a.decode && a.part_blocks ? a.num_parts : 1));
-  switch (a.decode ? a.waves : kPrefillWaves) {
-    case 2: prefill_mfma<QK, CK, D, 2><<<grid, dim3(64 * 2), 0, stream>>>(a); break;
-    case 4: prefill_mfma<QK, CK, D, 4><<<grid, dim3(64 * 4), 0, stream>>>(a); break;
-    case 8: prefill_mfma<QK, CK, D, 8><<<grid, dim3(64 * 8), 0, stream>>>(a); break;
+  switch (a.waves * 10 + a.wave_tiles) {
+    case 21: prefill_mfma<QK, CK, D, 2><<<grid, dim3(64 * 2), 0, stream>>>(a); break;
+    case 41: prefill_mfma<QK, CK, D, 4><<<grid, dim3(64 * 4), 0, stream>>>(a); break;
+    case 81: prefill_mfma<QK, CK, D, 8><<<grid, dim3(64 * 8), 0, stream>>>(a); break;
+    case 42: prefill_mfma<QK, CK, D, 4, 2><<<grid, dim3(64 * 4), 0, stream>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
