@@ -45,6 +45,25 @@ __device__ __forceinline__ void store_out(const DecodeArgs& a, int64_t elem, flo
   }
 }
 
+// Four consecutive output elements (elem a multiple of 4): one 16- or 8-byte
+// store when the output is aligned for it (the pointer is a kernel argument,
+// so the choice is uniform), else four element stores.
+__device__ __forceinline__ void store_out4(const DecodeArgs& a, int64_t elem, float4 v) {
+  if ((reinterpret_cast<uintptr_t>(a.out) & 15) != 0) {
+    store_out(a, elem, v.x);
+    store_out(a, elem + 1, v.y);
+    store_out(a, elem + 2, v.z);
+    store_out(a, elem + 3, v.w);
+  } else if (a.out_kind == kF32) {
+    *reinterpret_cast<float4*>(static_cast<float*>(a.out) + elem) = v;
+  } else {
+    const bool bf = a.out_kind == kBF16;
+    auto cv = [bf](float x) -> uint32_t { return bf ? f32_to_bf16_rne(x) : f32_to_f16_rne(x); };
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + elem) =
+        make_uint2(cv(v.x) | (cv(v.y) << 16), cv(v.z) | (cv(v.w) << 16));
+  }
+}
+
 // Merge the waves of a workgroup (each left its max, sum and unnormalised
 // output in LDS: s_acc is [kWaves][GT][D], s_ml is [kWaves][GT][2]) and write
 // the result, or the partition's partial result. The partition holds at least

@@ -145,6 +145,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma(const DecodeArgs a) {
   __shared__ float s_ml[kBalanced ? 1 : kWaves * GT * 2];
   __shared__ int s_pref[kBalanced ? kBalancedMaxSeqs + 1 : 1];
   __shared__ int s_shr[kBalanced ? kBalancedMaxSeqs : 1];  // shared-prefix blocks of each sequence
+  __shared__ int s_len[kBalanced ? kBalancedMaxSeqs : 1];  // context length of each sequence
   __shared__ int s_scan[kBalanced ? kWaves : 1];
 
   const int n_sub = kPrefix ? 1 : a.group / GT;  // the prefix pass: x is the KV head
@@ -573,6 +574,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma(const DecodeArgs a) {
         c = context_len(a, s);
         if (a.shared_prefix) shb = a.ws_shared[s];
         s_shr[s] = shb;
+        s_len[s] = c;
       }
       // Blocks past the shared prefix (those inside it were read by the prefix pass).
       nb[k] = c > 0 ? max(0, ((c + 15) >> 4) - shb) : 0;
@@ -651,7 +653,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma(const DecodeArgs a) {
       const int ps = s_pref[seq], pe = s_pref[seq + 1];
       const int piece_end = min(r_end, pe);
       const int shb = s_shr[seq];  // position ps is block shb of the sequence
-      ctx = context_len(a, seq);
+      ctx = s_len[seq];
       if (a.append && piece_end == pe) {  // this range holds the sequence's last block
         append_row<QK, CK, D, 64>(a, seq, kvh, lane);
         wait_own_stores();
@@ -671,39 +673,44 @@ __global__ __launch_bounds__(kThreads) void decode_mfma(const DecodeArgs a) {
       // A sequence with a shared prefix always leaves a piece: the merge adds the prefix pass's parts.
       const bool whole = pos == ps && piece_end == pe && shb == 0;
       const int64_t slot = seq + r;
+      // The results leave through the wave's V staging area (free between
+      // steps): the MFMA layout puts head 4g + i, column 16 db + n on lane
+      // (n, g), so direct stores would take NDB * 4 instructions of 16 to 64
+      // lanes each, and every vector memory instruction waits its turn behind
+      // the other waves' tile loads; restaged, each lane stores 16
+      // consecutive bytes and a 16-head tile takes D / 16 instructions.
+      float* const sf = reinterpret_cast<float*>(sv);
+      constexpr int RS = D + 4;  // staged row stride in floats: the four row groups fall on different banks
+      static_assert(GS * RS * 4 <= 2 * 16 * VS * 2, "staged rows fit the wave's V area");
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         float ls = lsum[t] + __shfl_xor(lsum[t], 16, 64);
         ls += __shfl_xor(ls, 32, 64);
         const int hb = h0 + 16 * t;  // first head of the sub-tile
-        if (whole) {
-          // The whole sequence: normalise and write the output rows 4g + i.
-          float inv[4];
+        float sc[4];  // the whole sequence: normalise; a piece: its unnormalised output
 #pragma unroll
-          for (int i = 0; i < 4; ++i) inv[i] = a.out_scale / __shfl(ls, 4 * g + i, 64);
+        for (int i = 0; i < 4; ++i) sc[i] = whole ? a.out_scale / __shfl(ls, 4 * g + i, 64) : a.out_scale;
+        wave_lds_fence();  // the last step's reads of the area, and the previous sub-tile's, are done
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            if (4 * g + i < GS) {
-              const int64_t row = ((int64_t)seq * a.num_heads + hb + 4 * g + i) * D;
+        for (int i = 0; i < 4; ++i) {
+          if (4 * g + i < GS) {
 #pragma unroll
-              for (int db = 0; db < NDB; ++db) store_out(a, row + db * 16 + n, acc[t][db][i] * inv[i]);
-            }
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            if (4 * g + i < GS) {
-              float* o = a.ws_out + ((int64_t)(hb + 4 * g + i) * slots + slot) * D;
-#pragma unroll
-              for (int db = 0; db < NDB; ++db) o[db * 16 + n] = acc[t][db][i] * a.out_scale;
-            }
-          }
-          if (g == 0 && n < GS) {
-            float* ml = a.ws_ml + ((int64_t)(hb + n) * slots + slot) * 2;
-            ml[0] = mref[t];
-            ml[1] = ls;
+            for (int db = 0; db < NDB; ++db) sf[(4 * g + i) * RS + db * 16 + n] = acc[t][db][i] * sc[i];
           }
         }
+        wave_lds_fence();
+        constexpr int kChunks = GS * D / 4;  // float4 chunks of the tile
+        static_assert(kChunks % 64 == 0, "whole rounds of the wave");
+#pragma unroll
+        for (int c = lane; c < kChunks; c += 64) {
+          const int hh = c / (D / 4);
+          const int col = (c - hh * (D / 4)) * 4;
+          const float4 v = *reinterpret_cast<const float4*>(sf + hh * RS + col);
+          if (whole) store_out4(a, ((int64_t)seq * a.num_heads + hb + hh) * D + col, v);
+          else *reinterpret_cast<float4*>(a.ws_out + ((int64_t)(hb + hh) * slots + slot) * D + col) = v;
+        }
+        if (!whole && g == 0 && n < GS)
+          *reinterpret_cast<float2*>(a.ws_ml + ((int64_t)(hb + n) * slots + slot) * 2) = make_float2(mref[t], ls);
       }
       pos = piece_end;
     }
