@@ -45,10 +45,13 @@ void wide_shape(int group, int& waves, int& wave_tiles) {
 }
 
 // Workgroups the wide decode aims at before it splits contexts: two per
-// compute unit, and for 2-wave workgroups four (measured on 64 sequences of
+// compute unit, whatever the workgroup's waves (measured on 64 sequences of
 // 32768 tokens over one KV head: 8-wave workgroups at two per unit 0.274 ms
-// against 0.306 ms at one; 2- and 4-wave workgroups slower beyond these).
-int64_t wide_target_workgroups(int waves) { return waves == 2 ? 1024 : 512; }
+// against 0.306 ms at one; 4-wave workgroups at G = 64 0.197 ms against 0.240
+// at one per unit and 0.214 at four; 2-wave workgroups at G = 32 0.182 ms
+// against 0.185 at four per unit and 0.214 at eight: more partitions leave
+// more partial results to write and merge).
+int64_t wide_target_workgroups(int) { return 512; }
 
 int choose_partition_blocks(int num_seqs, int num_heads, int num_kv_heads, int max_blocks) {
   const int group = num_heads / num_kv_heads;
