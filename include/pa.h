@@ -60,10 +60,12 @@ extern "C" {
 #endif
 
 typedef enum pa_dtype {
-  PA_DTYPE_F32 = 0,      /* IEEE binary32 */
-  PA_DTYPE_F16 = 1,      /* IEEE binary16 */
-  PA_DTYPE_BF16 = 2,     /* bfloat16 */
-  PA_DTYPE_FP8_E4M3 = 3  /* OCP OFP8 E4M3 (bias 7, max 448, NaN = S.1111.111); caches only */
+  PA_DTYPE_F32 = 0,       /* IEEE binary32 */
+  PA_DTYPE_F16 = 1,       /* IEEE binary16 */
+  PA_DTYPE_BF16 = 2,      /* bfloat16 */
+  PA_DTYPE_FP8_E4M3 = 3,  /* OCP OFP8 E4M3 (bias 7, max 448, NaN = S.1111.111); caches only */
+  PA_DTYPE_I32 = 4,       /* int32: index arrays, in tensor descriptors only */
+  PA_DTYPE_I64 = 5        /* int64: slot mappings, in tensor descriptors only */
 } pa_dtype;
 
 typedef enum pa_status {
@@ -425,6 +427,52 @@ int pa_bm_block_tables(const pa_block_manager* bm, const int64_t* seq_ids, int n
  */
 int pa_bm_shared_prefix(const pa_block_manager* bm, const int64_t* seq_ids, int n, int min_blocks,
                         int32_t* groups_out, int max_groups, int* num_groups);
+
+/*
+ * Tensor descriptors. pa_reshape_and_cache_t and pa_decode_t are
+ * pa_reshape_and_cache and pa_decode with every array given as a pa_tensor
+ * (pointer, dtype, shape, strides), so that the library itself checks that
+ * the arrays agree with one another before anything is queued: ranks, dense
+ * row-major strides (a dimension of size 1 may have any stride), equal
+ * shapes where the layouts above share a size, and the index dtypes. The
+ * sizes the flat calls take (num_tokens, num_seqs, num_heads, head_size,
+ * max_blocks_per_seq, num_blocks) come from the shapes; num_kv_heads and
+ * block_size must match the caches'. They then forward to the flat call,
+ * whose own checks and behaviour apply. Errors: PA_ERR_NULL (a NULL
+ * descriptor, or a NULL data pointer in a non-empty tensor), PA_ERR_SHAPE (a
+ * rank, stride or size that does not fit), PA_ERR_DTYPE (an index array that
+ * is not int32, or a slot mapping neither int32 nor int64), and those of the
+ * flat call.
+ */
+typedef struct pa_tensor {
+  void* data;         /* device memory */
+  pa_dtype dtype;
+  int32_t ndim;       /* 1 to 4 */
+  int64_t shape[4];   /* shape[0 .. ndim - 1] */
+  int64_t stride[4];  /* in elements */
+} pa_tensor;
+
+/*
+ *   key, value       [num_tokens, num_kv_heads, head_size], F32, F16 or BF16
+ *   k_cache, v_cache [num_blocks, num_kv_heads, block_size, head_size]
+ *   slot_mapping     [num_tokens], I32 or I64
+ * Other arguments as in pa_reshape_and_cache.
+ */
+int pa_reshape_and_cache_t(const pa_tensor* key, const pa_tensor* value, const pa_tensor* k_cache,
+                           const pa_tensor* v_cache, const pa_tensor* slot_mapping, float k_scale, float v_scale,
+                           void* stream);
+
+/*
+ *   out, q           [num_seqs, num_heads, head_size]
+ *   k_cache, v_cache [num_blocks, num_kv_heads, block_size, head_size]
+ *   block_tables     [num_seqs, max_blocks_per_seq], I32
+ *   context_lens     [num_seqs], I32
+ * Other arguments as in pa_decode (the library's own schedule, as there).
+ */
+int pa_decode_t(const pa_tensor* out, const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
+                const pa_tensor* block_tables, const pa_tensor* context_lens, float scale, int num_kv_heads,
+                int block_size, float k_scale, float v_scale, void* workspace, size_t workspace_bytes,
+                void* stream);
 
 /* Message for the last non-zero status returned on this thread ("" if none). */
 const char* pa_last_error(void);

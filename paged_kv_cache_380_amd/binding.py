@@ -17,10 +17,11 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("PA_LIB", os.path.join(_PKG, "libpa.so"))
 
 PA_DTYPE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2, torch.float8_e4m3fn: 3}
+PA_INDEX_DTYPE = {torch.int32: 4, torch.int64: 5}  # index arrays, in tensor descriptors only
 STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_DTYPE", 3: "PA_ERR_SHAPE", 4: "PA_ERR_UNSUPPORTED",
           5: "PA_ERR_WORKSPACE", 6: "PA_ERR_LAUNCH", 7: "PA_ERR_CAPACITY", 8: "PA_ERR_STATE"}
 
-EXPORTS = ("pa_reshape_and_cache", "pa_decode", "pa_decode_split", "pa_decode_workspace_bytes",
+EXPORTS = ("pa_reshape_and_cache", "pa_decode", "pa_reshape_and_cache_t", "pa_decode_t", "pa_decode_split", "pa_decode_workspace_bytes",
            "pa_decode_shared_prefix", "pa_decode_shared_prefix_workspace_bytes", "pa_decode_append",
            "pa_decode_partition_blocks", "pa_decode_scratch", "pa_decode_scratch_bytes", "pa_prefill", "pa_copy_blocks", "pa_bm_create", "pa_bm_destroy", "pa_bm_num_free_blocks",
            "pa_bm_block_refcount", "pa_bm_add_sequence", "pa_bm_fork", "pa_bm_free_sequence", "pa_bm_append_slots",
@@ -30,6 +31,26 @@ _lock = threading.Lock()
 _lib = None
 
 _vp, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+
+
+class PaTensor(ctypes.Structure):
+    """pa_tensor: pointer, dtype, rank, shape and strides (in elements) of one array."""
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int), ("ndim", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * 4), ("stride", ctypes.c_int64 * 4)]
+
+
+def tensor_desc(t: torch.Tensor) -> PaTensor:
+    """The pa_tensor of a torch tensor (its own shape and strides: the library checks them)."""
+    code = PA_DTYPE.get(t.dtype, PA_INDEX_DTYPE.get(t.dtype))
+    if code is None:
+        raise ValueError(f"unsupported dtype {t.dtype}")
+    if not 1 <= t.dim() <= 4:
+        raise ValueError("tensors of 1 to 4 dimensions")
+    d = PaTensor()
+    d.data, d.dtype, d.ndim = t.data_ptr(), code, t.dim()
+    for i in range(t.dim()):
+        d.shape[i], d.stride[i] = t.shape[i], t.stride(i)
+    return d
 
 
 class PAError(RuntimeError):
@@ -51,6 +72,11 @@ def load(path: str | None = None) -> ctypes.CDLL:
         lib.pa_reshape_and_cache.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i64, _i32, _i32, _i32,
                                              _f32, _f32, _vp]
         lib.pa_reshape_and_cache.restype = _i32
+        desc = ctypes.POINTER(PaTensor)
+        lib.pa_reshape_and_cache_t.argtypes = [desc] * 5 + [_f32, _f32, _vp]
+        lib.pa_reshape_and_cache_t.restype = _i32
+        lib.pa_decode_t.argtypes = [desc] * 6 + [_f32, _i32, _i32, _f32, _f32, _vp, _sz, _vp]
+        lib.pa_decode_t.restype = _i32
         dec = [_vp, _vp, _vp, _vp, _vp, _vp, _f32, _i32, _i32, _i32, _i32, _i32, _i32, _i64, _i32, _i32, _i32, _f32,
                _f32]
         lib.pa_decode.argtypes = dec + [_vp, _sz, _vp]
@@ -152,6 +178,29 @@ def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, k_scale: float
         _ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping),
         int(slot_mapping.dtype == torch.int64), T, Hkv, D, N, B, _dtype(key), _dtype(k_cache),
         float(k_scale), float(v_scale), _stream(key, stream)))
+
+
+def reshape_and_cache_t(key, value, k_cache, v_cache, slot_mapping, k_scale: float = 1.0, v_scale: float = 1.0,
+                        stream=None) -> None:
+    """pa_reshape_and_cache_t: reshape_and_cache with the arrays passed as descriptors (the library checks them)."""
+    lib = load()
+    ds = [tensor_desc(x) for x in (key, value, k_cache, v_cache, slot_mapping)]
+    _check(lib, lib.pa_reshape_and_cache_t(*[ctypes.byref(d) for d in ds], float(k_scale), float(v_scale),
+                                           _stream(key, stream)))
+
+
+def decode_t(out, q, k_cache, v_cache, block_tables, context_lens, scale: float, num_kv_heads: int,
+             block_size: int = 16, k_scale: float = 1.0, v_scale: float = 1.0, workspace: torch.Tensor | None = None,
+             stream=None) -> torch.Tensor:
+    """pa_decode_t: decode with the arrays passed as descriptors (the library checks them)."""
+    lib = load()
+    ds = [tensor_desc(x) for x in (out, q, k_cache, v_cache, block_tables, context_lens)]
+    if workspace is None:
+        workspace = workspace_for(q, num_kv_heads, block_tables)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib, lib.pa_decode_t(*[ctypes.byref(d) for d in ds], float(scale), num_kv_heads, block_size,
+                                float(k_scale), float(v_scale), _ptr(workspace), ws_bytes, _stream(q, stream)))
+    return out
 
 
 def decode_workspace_bytes(num_seqs: int, num_heads: int, num_kv_heads: int, head_size: int,

@@ -271,3 +271,98 @@ def test_decode_append_rejects(lib, kw, code):
 
 def test_decode_append_zero_seqs_is_a_no_op(lib):
     assert append(lib, S=0, out=None, q=None, key=None, value=None, slots=None) == 0
+
+
+# --- tensor descriptors (pa_reshape_and_cache_t, pa_decode_t) ---------------------------------------
+
+def desc(shape, dtype, data=FAKE, stride=None):
+    """A pa_tensor of the given shape (dense row-major unless stride is given) at a fake address."""
+    d = binding.PaTensor()
+    d.data, d.dtype, d.ndim = data, dtype, len(shape)
+    run = 1
+    strides = [0] * len(shape)
+    for i in reversed(range(len(shape))):
+        strides[i] = run
+        run *= shape[i]
+    for i, n in enumerate(shape):
+        d.shape[i] = n
+        d.stride[i] = strides[i] if stride is None else stride[i]
+    return d
+
+
+F16, I32, I64, F32 = 1, 4, 5, 0
+
+
+def reshape_t(lib, **kw):
+    a = dict(key=desc([4, 2, 128], F16), value=desc([4, 2, 128], F16), kc=desc([8, 2, 16, 128], F16),
+             vc=desc([8, 2, 16, 128], F16), slots=desc([4], I64), ks=1.0, vs=1.0)
+    a.update(kw)
+    ref = [None if a[k] is None else ctypes.byref(a[k]) for k in ("key", "value", "kc", "vc", "slots")]
+    return lib.pa_reshape_and_cache_t(*ref, a["ks"], a["vs"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(key=None), 1),                                            # NULL descriptor
+    (dict(key=desc([4, 256], F16)), 3),                             # rank
+    (dict(key=desc([4, 2, 128], F16, stride=[512, 128, 2])), 3),    # not dense
+    (dict(value=desc([4, 2, 64], F16)), 3),                         # key and value shapes
+    (dict(value=desc([4, 2, 128], 2)), 2),                          # key and value dtypes
+    (dict(kc=desc([8, 4, 16, 128], F16), vc=desc([8, 4, 16, 128], F16)), 3),  # cache KV heads
+    (dict(vc=desc([9, 2, 16, 128], F16)), 3),                       # cache shapes
+    (dict(slots=desc([3], I64)), 3),                                # tokens
+    (dict(slots=desc([4], F32)), 2),                                # slot dtype
+    (dict(key=desc([4, 2, 128], F16, data=0)), 1),                  # no data
+    (dict(key=desc([4, 2, 128], I32), value=desc([4, 2, 128], I32)), 2),  # forwarded: key dtype
+    (dict(kc=desc([8, 2, 8, 128], F16), vc=desc([8, 2, 8, 128], F16)), 4),  # forwarded: block size
+])
+def test_reshape_t_rejects(lib, kw, code):
+    assert reshape_t(lib, **kw) == code
+    assert lib.pa_last_error().decode()
+
+
+def test_reshape_t_zero_tokens_is_a_no_op(lib):
+    assert reshape_t(lib, key=desc([0, 2, 128], F16, data=0), value=desc([0, 2, 128], F16, data=0),
+                     slots=desc([0], I32, data=0)) == 0
+
+
+def decode_t(lib, **kw):
+    a = dict(out=desc([4, 8, 128], F16), q=desc([4, 8, 128], F16), kc=desc([64, 2, 16, 128], F16),
+             vc=desc([64, 2, 16, 128], F16), bt=desc([4, 8], I32), cl=desc([4], I32), Hkv=2, B=16, ws=None, wsb=0)
+    a.update(kw)
+    ref = [None if a[k] is None else ctypes.byref(a[k]) for k in ("out", "q", "kc", "vc", "bt", "cl")]
+    return lib.pa_decode_t(*ref, 0.125, a["Hkv"], a["B"], 1.0, 1.0, a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cl=None), 1),                                             # NULL descriptor
+    (dict(out=desc([4, 8, 64], F16)), 3),                           # out and q shapes
+    (dict(q=desc([4, 8, 128], F16, stride=[2048, 256, 1])), 3),     # not dense
+    (dict(Hkv=4), 3),                                               # num_kv_heads vs the caches
+    (dict(B=8), 3),                                                 # block_size vs the caches
+    (dict(kc=desc([64, 2, 16, 64], F16), vc=desc([64, 2, 16, 64], F16)), 3),  # head sizes
+    (dict(bt=desc([5, 8], I32)), 3),                                # table rows
+    (dict(cl=desc([3], I32)), 3),                                   # context lengths
+    (dict(bt=desc([4, 8], I64)), 2),                                # table dtype
+    (dict(vc=desc([64, 2, 16, 128], 3)), 2),                        # cache dtypes differ
+    (dict(out=desc([4, 8, 128], 2)), 2),                            # forwarded: out dtype
+    (dict(q=desc([4, 6, 128], F16), out=desc([4, 6, 128], F16), Hkv=4,
+          kc=desc([64, 4, 16, 128], F16), vc=desc([64, 4, 16, 128], F16)), 3),  # forwarded: 6 % 4
+])
+def test_decode_t_rejects(lib, kw, code):
+    assert decode_t(lib, **kw) == code
+    assert lib.pa_last_error().decode()
+
+
+def test_decode_t_zero_seqs_is_a_no_op(lib):
+    assert decode_t(lib, out=desc([0, 8, 128], F16, data=0), q=desc([0, 8, 128], F16, data=0),
+                    bt=desc([0, 8], I32, data=0), cl=desc([0], I32, data=0)) == 0
+
+
+def test_tensor_desc_of_a_torch_tensor():
+    import torch
+    t = torch.zeros(3, 4, 5, dtype=torch.bfloat16)
+    d = binding.tensor_desc(t)
+    assert (d.dtype, d.ndim, list(d.shape[:3]), list(d.stride[:3])) == (2, 3, [3, 4, 5], [20, 5, 1])
+    d = binding.tensor_desc(t.transpose(0, 1))  # the descriptor keeps the view's strides: the library refuses it
+    assert list(d.stride[:3]) == [5, 20, 1]
+    assert binding.tensor_desc(torch.zeros(2, dtype=torch.int64)).dtype == 5
