@@ -694,7 +694,7 @@ __global__ __launch_bounds__(64) void decode_reduce(const DecodeArgs a) {
 // Merge the pieces of every (sequence, head) that the balanced schedule of
 // the matrix-core kernel cut: ranges r_lo .. r_hi (those of them that hold
 // any block) each left one piece in slot seq + r. With the shared-prefix
-// pass, a sequence inside a group also has one part per kPrefixPartBlocks
+// pass, a sequence inside a group also has one part per a.prefix_part_blocks
 // shared blocks, merged in after the pieces. Sequences held by a single
 // range and outside every group were written by the kernel itself; empty
 // ones get zeros here.
@@ -710,7 +710,7 @@ __global__ __launch_bounds__(64) void decode_bal_reduce(const DecodeArgs a) {
   const int64_t sh = (int64_t)seq * a.num_heads + h;
   const int shb = a.shared_prefix ? a.ws_shared[seq] : 0;  // shared blocks, merged from the prefix pass
   // The prefix pass's first part (its only one for prefixes of at most
-  // kPrefixPartBlocks blocks), loaded in the same round as the indices above
+  // a.prefix_part_blocks blocks), loaded in the same round as the indices above
   // (its address does not depend on them; the slot exists for every sequence).
   float pm0 = kNegInf, pl0 = 0.f, po0[D / 64];
   if (a.shared_prefix) {
@@ -813,7 +813,7 @@ __global__ __launch_bounds__(64) void decode_bal_reduce(const DecodeArgs a) {
   }
   if (shb > 0) {
     // The prefix pass's parts: rescale what the pieces gave to the joint max.
-    const int np = (shb + kPrefixPartBlocks - 1) / kPrefixPartBlocks;
+    const int np = (shb + a.prefix_part_blocks - 1) / a.prefix_part_blocks;
     const int64_t p0 = ((int64_t)h * a.num_seqs + seq) * a.prefix_parts;
     const float* pml = a.ws_sh_ml + 2 * p0;
     const float* po = a.ws_sh_out + p0 * D;

@@ -30,7 +30,7 @@
 //    that share their first blocks ("vLLM 前世今生" §3.2: a common prompt in
 //    the same physical blocks), so every shared K/V tile is read and
 //    multiplied once for all of them; workgroups are (KV head, part of
-//    kPrefixPartBlocks shared blocks, tile) and leave per-part partial
+//    a.prefix_part_blocks shared blocks, tile) and leave per-part partial
 //    results for decode_bal_reduce.
 // In all, a wave keeps the next blocks' K/V loads in flight while it works.
 //
@@ -441,9 +441,9 @@ __global__ __launch_bounds__(kThreads) void decode_mfma(const DecodeArgs a) {
     const int s0 = a.grp_first[gi] + (tile - a.grp_tile0[gi]) * spt;
     const int s_end = min(a.grp_first[gi] + a.grp_count[gi], s0 + spt);
     const int nshared = a.grp_blocks[gi];
-    blk0 = part * kPrefixPartBlocks;
+    blk0 = part * a.prefix_part_blocks;
     if (blk0 >= nshared || s0 >= s_end) return;
-    const int nblk = min(kPrefixPartBlocks, nshared - blk0);
+    const int nblk = min(a.prefix_part_blocks, nshared - blk0);
     ctx = nshared * 16;
     const int32_t* bt = a.block_tables + (int64_t)a.grp_first[gi] * a.max_blocks + blk0;
     for (int j = tid; j < nblk; j += kThreads) s_blocks[j] = bt[j];

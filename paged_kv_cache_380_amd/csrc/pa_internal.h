@@ -25,7 +25,9 @@ struct ReshapeArgs {
 // Returns a hipError_t of the launch.
 hipError_t launch_reshape(const ReshapeArgs& a, int src_kind, int cache_kind, hipStream_t stream);
 
-// Groups a shared-prefix call may name, and blocks per part of the prefix kernel.
+// Groups a shared-prefix call may name, and the shortest part (in blocks) of
+// the prefix kernel, for which the workspace is sized; a call takes parts of
+// up to kMaxPartitionBlocks blocks (prefix_part_blocks).
 constexpr int kMaxPrefixGroups = 16;
 constexpr int kPrefixPartBlocks = 64;
 
@@ -65,7 +67,8 @@ struct DecodeArgs {
   // only the blocks past each sequence's shared prefix.
   int shared_prefix;      // 1: the pass runs (ws_shared, ws_sh_* and the group list are set)
   int prefix_groups;      // number of groups (<= kMaxPrefixGroups)
-  int prefix_parts;       // P1: parts of kPrefixPartBlocks blocks of the longest shared prefix
+  int prefix_parts;       // P1: parts of prefix_part_blocks blocks of the longest shared prefix
+  int prefix_part_blocks; // blocks per part (a power of two from kPrefixPartBlocks to kMaxPartitionBlocks)
   int* ws_shared;         // [S] shared blocks of each sequence (0 outside every group)
   float* ws_sh_out;       // [H, S, P1, D] unnormalised partial outputs over the shared blocks
   float* ws_sh_ml;        // [H, S, P1, 2] their max (log2 domain) and sum

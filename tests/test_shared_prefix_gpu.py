@@ -10,7 +10,8 @@ checked against the oracle (at the usual tolerance) and against pa_decode at
 twice or never cannot hide. Cases: groups anywhere in the batch (sequences
 reordered), groups whose size is not a multiple of the sequences per tile,
 16 / 8 / 4 query heads per KV head (1, 2 and 4 sequences per tile), shared
-prefixes that are not a multiple of the pass's 64-block parts, a group named
+prefixes that are not a multiple of the pass's parts (64 blocks, or 256 and
+512 where the call has the sequences to keep 512 workgroups), a group named
 shorter than the blocks its members really share, single-sequence groups
 whose private part is empty or only a masked tail, FP8, bf16 and f16 caches,
 head size 64, and the prefix-sharing FP8 batch at full size.
@@ -179,6 +180,29 @@ def test_prefix_long_fp8_full_size_sampled():
     ref = oracle_decode(w, kc, vc, seqs=seqs)
     got = out.cpu().numpy()[seqs]
     assert float(np.abs(got - ref[seqs]).max()) <= tolerance(w)  # the oracle fills only the sampled rows
+
+
+@pytest.mark.parametrize("seqs,shared", [(256, 600), (128, 300)])
+def test_long_parts(seqs, shared):
+    # Parts longer than 64 blocks, where the call still gives 512 workgroups: 256 sequences (64 tiles of 4
+    # per KV head) on 600 shared blocks take parts of 512 (the second of 88 blocks); 128 sequences on 300
+    # take parts of 256 (the second of 44). Every sequence against pa_decode, sampled ones against the oracle.
+    from paged_kv_cache_380_amd import binding
+    rng = np.random.default_rng(31 + seqs)
+    w = sharing(f"shared_long_parts_{seqs}", 32, 8, 128, "bf16", "fp8_e4m3", shared,
+                [int(rng.integers(1, 100)) for _ in range(seqs)], [], seed=33)
+    case = GpuCase(w)
+    case.append()
+    ref_gpu = case.decode(out_dtype=torch.float32)
+    out = torch.full(case.q.shape, float("nan"), dtype=torch.float32, device="cuda")
+    binding.decode_shared_prefix(out, case.q, case.kc, case.vc, case.tables, case.lens, w.scale, w.num_kv_heads,
+                                 [(0, seqs, shared)], w.block_size, w.k_scale, w.v_scale)
+    torch.cuda.synchronize()
+    assert float((out - ref_gpu).abs().max()) <= 1e-4
+    sample = [0, 3, seqs // 2 + 1, seqs - 1]
+    kc, vc = oracle_fill(w)
+    ref = oracle_decode(w, kc, vc, seqs=sample)
+    assert float(np.abs(out.cpu().numpy()[sample] - ref[sample]).max()) <= tolerance(w)
 
 
 def test_groups_ignored_past_the_balanced_batch_and_for_float32():
