@@ -628,14 +628,11 @@ __global__ __launch_bounds__(kThreads) void decode_gqa(const DecodeArgs a) {
   finish_partition<GT, D>(a, &s_acc[0][0][0], &s_ml[0][0][0], seq, h0, part, seq_parts, tid);
 }
 
-// Merge the partitions of every (sequence, head) whose context spans several.
-// Up to 64 partitions take one round of loads: lane p reads partition p's
-// max and sum, every lane its columns of the first kPre partitions' outputs;
-// the weights are then shared by lane reads (partitions past kPre, and past
-// 64, are read in further rounds). The merge order is fixed: deterministic.
+// Merge the partitions of every (sequence, head) whose context spans several:
+// up to 64 partitions in one or two rounds of 16-byte loads (below), more one
+// partition at a time. The merge order is fixed: deterministic.
 template <int D>
 __global__ __launch_bounds__(64) void decode_reduce(const DecodeArgs a) {
-  constexpr int kPre = 16;
   const int h = blockIdx.x;
   const int seq = blockIdx.y;
   const int lane = threadIdx.x;
@@ -645,48 +642,70 @@ __global__ __launch_bounds__(64) void decode_reduce(const DecodeArgs a) {
   const int64_t base = ((int64_t)seq * a.num_heads + h) * a.num_parts;
   const float* ml = a.ws_ml + 2 * base;
   const float* o = a.ws_out + base * D;
+  const int64_t sh = (int64_t)seq * a.num_heads + h;
+  if (seq_parts <= 64) {
+    // Lane p holds partition p's (max, sum); the outputs are read as 16-byte
+    // chunks, PPI partitions per wave instruction (lane (c, sp) takes chunk c
+    // of partition PPI * j + sp), kRound instructions in flight at a time, so
+    // that 64 partitions take two rounds of loads rather than one per
+    // partition; lanes holding the same chunk then add up by shuffles.
+    constexpr int CH = D / 4;       // 16-byte chunks per output row
+    constexpr int PPI = 64 / CH;    // partitions per wave instruction
+    constexpr int kRound = 16;
+    const int c = lane % CH, sp = lane / CH;
+    const bool mine = lane < seq_parts;
+    const float2 mlv = mine ? *reinterpret_cast<const float2*>(ml + 2 * lane) : make_float2(kNegInf, 0.f);
+    float M = mlv.x;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+    const float f = mine ? fast_exp2(mlv.x - M) : 0.f;
+    float L = mlv.y * f;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off, 64);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    const int nj = (seq_parts + PPI - 1) / PPI;  // instructions needed
+    for (int j0 = 0; j0 < nj; j0 += kRound) {
+      float4 v[kRound];
+      float w[kRound];
+#pragma unroll
+      for (int u = 0; u < kRound; ++u) {
+        const int p = PPI * (j0 + u) + sp;
+        const int pc = p < seq_parts ? p : 0;  // past the last partition: a valid row, weight 0
+        v[u] = *reinterpret_cast<const float4*>(o + (int64_t)pc * D + 4 * c);
+        w[u] = __shfl(f, pc, 64) * (p < seq_parts ? 1.f : 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < kRound; ++u) {
+        acc.x += v[u].x * w[u];
+        acc.y += v[u].y * w[u];
+        acc.z += v[u].z * w[u];
+        acc.w += v[u].w * w[u];
+      }
+    }
+#pragma unroll
+    for (int off = CH; off < 64; off <<= 1) {
+      acc.x += __shfl_xor(acc.x, off, 64);
+      acc.y += __shfl_xor(acc.y, off, 64);
+      acc.z += __shfl_xor(acc.z, off, 64);
+      acc.w += __shfl_xor(acc.w, off, 64);
+    }
+    if (sp == 0) {
+      const float inv = 1.f / L;
+      store_out4(a, sh * D + 4 * c, make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv));
+    }
+    return;
+  }
   float O[D / 64];
 #pragma unroll
   for (int k = 0; k < D / 64; ++k) O[k] = 0.f;
   float M = kNegInf, L = 0.f;
-  if (seq_parts <= 64) {
-    float ov[kPre][D / 64];
+  for (int p = 0; p < seq_parts; ++p) M = fmaxf(M, ml[2 * p]);
+  for (int p = 0; p < seq_parts; ++p) {
+    const float f = fast_exp2(ml[2 * p] - M);
+    L += ml[2 * p + 1] * f;
 #pragma unroll
-    for (int j = 0; j < kPre; ++j)
-#pragma unroll
-      for (int k = 0; k < D / 64; ++k) ov[j][k] = j < seq_parts ? o[(int64_t)j * D + lane + 64 * k] : 0.f;
-    const bool mine = lane < seq_parts;
-    const float m = mine ? ml[2 * lane] : kNegInf;
-    const float l = mine ? ml[2 * lane + 1] : 0.f;
-    M = m;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
-    const float f = mine ? fast_exp2(m - M) : 0.f;
-    L = l * f;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off, 64);
-#pragma unroll
-    for (int j = 0; j < kPre; ++j) {
-      const float fj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), j));
-#pragma unroll
-      for (int k = 0; k < D / 64; ++k) O[k] += ov[j][k] * fj;
-    }
-#pragma unroll 4
-    for (int j = kPre; j < seq_parts; ++j) {
-      const float fj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), j));
-#pragma unroll
-      for (int k = 0; k < D / 64; ++k) O[k] += o[(int64_t)j * D + lane + 64 * k] * fj;
-    }
-  } else {
-    for (int p = 0; p < seq_parts; ++p) M = fmaxf(M, ml[2 * p]);
-    for (int p = 0; p < seq_parts; ++p) {
-      const float f = fast_exp2(ml[2 * p] - M);
-      L += ml[2 * p + 1] * f;
-#pragma unroll
-      for (int k = 0; k < D / 64; ++k) O[k] += o[(int64_t)p * D + lane + 64 * k] * f;
-    }
+    for (int k = 0; k < D / 64; ++k) O[k] += o[(int64_t)p * D + lane + 64 * k] * f;
   }
-  const int64_t sh = (int64_t)seq * a.num_heads + h;
 #pragma unroll
   for (int k = 0; k < D / 64; ++k) store_out(a, sh * D + lane + 64 * k, O[k] / L);
 }
