@@ -646,12 +646,11 @@ __global__ __launch_bounds__(64) void decode_reduce(const DecodeArgs a) {
   if (seq_parts <= 64) {
     // Lane p holds partition p's (max, sum); the outputs are read as 16-byte
     // chunks, PPI partitions per wave instruction (lane (c, sp) takes chunk c
-    // of partition PPI * j + sp), kRound instructions in flight at a time, so
+    // of partition PPI * j + sp), 4 or 16 instructions in flight at a time, so
     // that 64 partitions take two rounds of loads rather than one per
     // partition; lanes holding the same chunk then add up by shuffles.
     constexpr int CH = D / 4;       // 16-byte chunks per output row
     constexpr int PPI = 64 / CH;    // partitions per wave instruction
-    constexpr int kRound = 16;
     const int c = lane % CH, sp = lane / CH;
     const bool mine = lane < seq_parts;
     const float2 mlv = mine ? *reinterpret_cast<const float2*>(ml + 2 * lane) : make_float2(kNegInf, 0.f);
@@ -664,24 +663,31 @@ __global__ __launch_bounds__(64) void decode_reduce(const DecodeArgs a) {
     for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off, 64);
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     const int nj = (seq_parts + PPI - 1) / PPI;  // instructions needed
-    for (int j0 = 0; j0 < nj; j0 += kRound) {
-      float4 v[kRound];
-      float w[kRound];
+    // Rounds of K instructions in flight: 4 when that covers every partition
+    // (the common few-partition case issues no idle loads), else 16.
+    auto rounds = [&](auto k_c) {
+      constexpr int K = decltype(k_c)::value;
+      for (int j0 = 0; j0 < nj; j0 += K) {
+        float4 v[K];
+        float w[K];
 #pragma unroll
-      for (int u = 0; u < kRound; ++u) {
-        const int p = PPI * (j0 + u) + sp;
-        const int pc = p < seq_parts ? p : 0;  // past the last partition: a valid row, weight 0
-        v[u] = *reinterpret_cast<const float4*>(o + (int64_t)pc * D + 4 * c);
-        w[u] = __shfl(f, pc, 64) * (p < seq_parts ? 1.f : 0.f);
-      }
+        for (int u = 0; u < K; ++u) {
+          const int p = PPI * (j0 + u) + sp;
+          const int pc = p < seq_parts ? p : 0;  // past the last partition: a valid row, weight 0
+          v[u] = *reinterpret_cast<const float4*>(o + (int64_t)pc * D + 4 * c);
+          w[u] = __shfl(f, pc, 64) * (p < seq_parts ? 1.f : 0.f);
+        }
 #pragma unroll
-      for (int u = 0; u < kRound; ++u) {
-        acc.x += v[u].x * w[u];
-        acc.y += v[u].y * w[u];
-        acc.z += v[u].z * w[u];
-        acc.w += v[u].w * w[u];
+        for (int u = 0; u < K; ++u) {
+          acc.x += v[u].x * w[u];
+          acc.y += v[u].y * w[u];
+          acc.z += v[u].z * w[u];
+          acc.w += v[u].w * w[u];
+        }
       }
-    }
+    };
+    if (nj <= 4) rounds(std::integral_constant<int, 4>{});
+    else rounds(std::integral_constant<int, 16>{});
 #pragma unroll
     for (int off = CH; off < 64; off <<= 1) {
       acc.x += __shfl_xor(acc.x, off, 64);
