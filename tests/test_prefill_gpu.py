@@ -116,6 +116,9 @@ def test_empty_and_cut_chunks():
     assert np.abs(got[:4] - ref[:4]).max() <= 2e-3
     assert np.abs(got[4:10] - ref[4:10]).max() <= 2e-3     # first 6 rows of the 9-token chunk
     assert np.isnan(got[10:]).all()                         # rows past max_query_len are not written
+    native = run(case, q, starts, 6, out_dtype=torch.bfloat16).float().cpu()  # the 16-bit output's own store path
+    assert torch.equal(native[:10], torch.from_numpy(got[:10]).to(torch.bfloat16).float())
+    assert torch.isnan(native[10:]).all()
 
 
 def test_prefill_benchmark_size():
