@@ -433,7 +433,8 @@ int pa_bm_shared_prefix(const pa_block_manager* bm, const int64_t* seq_ids, int 
  * pa_reshape_and_cache and pa_decode with every array given as a pa_tensor
  * (pointer, dtype, shape, strides), so that the library itself checks that
  * the arrays agree with one another before anything is queued: ranks, dense
- * row-major strides (a dimension of size 1 may have any stride), equal
+ * row-major strides (a dimension of size 1 may have any stride; an empty
+ * tensor's strides are not looked at), element counts below 2^62, equal
  * shapes where the layouts above share a size, and the index dtypes. The
  * sizes the flat calls take (num_tokens, num_seqs, num_heads, head_size,
  * max_blocks_per_seq, num_blocks) come from the shapes; num_kv_heads and

@@ -10,21 +10,28 @@ namespace {
 
 using pa::fail;
 
-// A descriptor of the given rank, dense row-major (a size-1 dimension may have
-// any stride), with non-negative sizes and data for a non-empty tensor.
+// A descriptor of the given rank with non-negative sizes whose element count
+// fits 2^62; if it is not empty, dense row-major (a size-1 dimension may have
+// any stride) and with data. An empty tensor's strides are not looked at.
 int check_tensor(const pa_tensor* t, const char* call, const char* name, int ndim) {
   if (!t) return fail(PA_ERR_NULL, "%s: NULL descriptor for %s", call, name);
   if (t->ndim != ndim) return fail(PA_ERR_SHAPE, "%s: %s has %d dimensions, expected %d", call, name, t->ndim, ndim);
-  int64_t expect = 1, elems = 1;
-  for (int i = ndim - 1; i >= 0; --i) {
+  int64_t elems = 1;
+  for (int i = 0; i < ndim; ++i) {
     if (t->shape[i] < 0) return fail(PA_ERR_SHAPE, "%s: %s has a negative size", call, name);
+    if (t->shape[i] > 0 && elems > (INT64_C(1) << 62) / t->shape[i])
+      return fail(PA_ERR_SHAPE, "%s: %s has too many elements", call, name);
+    elems *= t->shape[i];
+  }
+  if (elems == 0) return PA_OK;
+  int64_t expect = 1;
+  for (int i = ndim - 1; i >= 0; --i) {
     if (t->shape[i] != 1 && t->stride[i] != expect)
       return fail(PA_ERR_SHAPE, "%s: %s must be dense row-major (dimension %d has stride %lld, expected %lld)", call,
                   name, i, (long long)t->stride[i], (long long)expect);
     expect *= t->shape[i];
-    elems *= t->shape[i];
   }
-  if (elems > 0 && !t->data) return fail(PA_ERR_NULL, "%s: %s has no data", call, name);
+  if (!t->data) return fail(PA_ERR_NULL, "%s: %s has no data", call, name);
   return PA_OK;
 }
 

@@ -320,6 +320,15 @@ def test_reshape_t_rejects(lib, kw, code):
     assert lib.pa_last_error().decode()
 
 
+def test_tensor_desc_huge_and_empty_strides(lib):
+    # an element count past 2^62 is refused before any product can overflow; an empty tensor's strides are
+    # not looked at
+    assert reshape_t(lib, key=desc([1 << 40, 1 << 20, 128], F16, stride=[1, 1, 1]),
+                     value=desc([1 << 40, 1 << 20, 128], F16, stride=[1, 1, 1])) == 3
+    assert reshape_t(lib, key=desc([0, 2, 128], F16, data=0, stride=[7, 7, 7]),
+                     value=desc([0, 2, 128], F16, data=0, stride=[7, 7, 7]), slots=desc([0], I64, data=0)) == 0
+
+
 def test_reshape_t_zero_tokens_is_a_no_op(lib):
     assert reshape_t(lib, key=desc([0, 2, 128], F16, data=0), value=desc([0, 2, 128], F16, data=0),
                      slots=desc([0], I32, data=0)) == 0
