@@ -159,3 +159,21 @@ def test_prefill_benchmark_size():
     print(f"[prefill] 8 x 2048 benchmark launch, {len(rows)} rows against the oracle: max|err|={err:.3e}",
           flush=True)
     assert err <= tolerance(w), err
+
+
+@pytest.mark.parametrize("case", range(32))
+def test_prefill_sweep(case):
+    # Seeded draws: 1 to 8 sequences with contexts of 1 to 3000 tokens and chunks from one token to the whole
+    # prompt, a head layout from MHA to 16 query heads per KV head, head size 64 or 128, 16-bit queries over
+    # 16-bit or FP8 caches, against the oracle (and the native output against the rounded float32 one).
+    rng = np.random.default_rng(500 + case)
+    H, Hkv = [(8, 8), (8, 2), (12, 3), (32, 8), (16, 1), (32, 4)][int(rng.integers(6))]
+    dtype, cache = COMBOS[int(rng.integers(len(COMBOS)))]
+    D = int(rng.choice([64, 128]))
+    S = int(rng.integers(1, 9))
+    lens = [int(rng.integers(1, int(rng.choice([50, 500, 3000])) + 1)) for _ in range(S)]
+    qlens = [int(rng.choice([1, L, int(rng.integers(1, L + 1))])) for L in lens]
+    print(f"[prefill sweep] case {case}: {H}/{Hkv} heads D {D} {dtype}/{cache} lens {lens} chunks {qlens}",
+          flush=True)
+    w, case_, q, starts = make(f"pf_sweep{case}", lens, qlens, H, Hkv, D, dtype, cache, seed=600 + case)
+    check(w, case_, q, starts, f"sweep {case}")
